@@ -1,0 +1,209 @@
+"""Pins that tie the CPU oracle to facts other than itself.
+
+Each pin takes a loaded oracle library (ctypes handle) and raises AssertionError when the
+oracle disagrees with:
+  - the IEEE binary32 layout of bf16 (exhaustive over all 65,536 patterns, against
+    torch's own bf16 -> float64 conversion, plus textbook values);
+  - closed forms whose exact result is known without summing anything
+    (identity W, one-hot x, constant W with small-integer x);
+  - the exact rational value of the sum (fractions.Fraction brute force on tiny shapes,
+    where fp64 summation must land within the standard recursive-summation bound
+    gamma_K * sum|terms|, gamma_K = K u / (1 - K u), u = 2^-53);
+  - an independent library routine (numpy float64 matmul) at the working shapes.
+
+The mutation test in test_oracle.py compiles deliberately broken copies of the oracle and
+checks that at least one pin rejects each of them.
+"""
+from __future__ import annotations
+
+import math
+import sys
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+
+U53 = 2.0 ** -53
+
+
+def gamma(n: int, u: float = U53) -> float:
+    return n * u / (1.0 - n * u)
+
+
+def _rand_bits(rng: np.random.Generator, shape, scale=1.0, wide_exponents=False):
+    """Finite bf16 bit patterns: normal values, optionally spread over many binades."""
+    v = rng.standard_normal(shape).astype(np.float32) * np.float32(scale)
+    if wide_exponents:
+        v *= np.exp2(rng.integers(-24, 25, size=shape)).astype(np.float32)
+    t = torch.from_numpy(v).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _exact(bits) -> list:
+    """Exact rational values of finite bf16 bits, via the binary32 layout by hand."""
+    out = []
+    for b in np.asarray(bits, dtype=np.uint16).ravel().tolist():
+        sign = -1 if b & 0x8000 else 1
+        e = (b >> 7) & 0xFF
+        f = b & 0x7F
+        assert e != 0xFF, "finite inputs only"
+        if e == 0:
+            val = Fraction(f, 1 << 7) * Fraction(1, 1 << 126)
+        else:
+            val = (1 + Fraction(f, 1 << 7)) * (Fraction(2) ** (e - 127))
+        out.append(sign * val)
+    return out
+
+
+# --------------------------------------------------------------------------- decode
+def pin_bf16_decode(so):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_to_f64(bits, so=so)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    nan_g, nan_r = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(nan_g, nan_r), "NaN patterns differ"
+    ok = ~nan_r
+    assert np.array_equal(got[ok], ref[ok]), "decoded values differ from torch"
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok])), "signs of zero differ"
+    textbook = {0x3F80: 1.0, 0xC000: -2.0, 0x3C80: 2.0 ** -6, 0x0001: 2.0 ** -133,
+                0x0080: 2.0 ** -126, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127, 0x7F80: math.inf,
+                0xFF80: -math.inf, 0x8000: -0.0}
+    for b, v in textbook.items():
+        g = got[b]
+        assert g == v and math.copysign(1, g) == math.copysign(1, v), hex(b)
+
+
+# --------------------------------------------------------------------------- closed forms
+def pin_identity(so):
+    rng = np.random.default_rng(11)
+    for n in (1, 129, 1024):
+        w = np.zeros((n, n), dtype=np.uint16)
+        w[np.arange(n), np.arange(n)] = 0x3F80
+        x = _rand_bits(rng, (n,))
+        y, s = oracle.gemv(w, x, so=so)
+        xv = oracle.bf16_to_f64(x, so=so)
+        assert np.array_equal(y[0], xv), f"identity {n}"
+        assert np.array_equal(s[0], np.abs(xv)), f"identity s_abs {n}"
+
+
+def pin_one_hot(so):
+    rng = np.random.default_rng(12)
+    for n, k in ((7, 129), (33, 1000), (64, 4096)):
+        w = _rand_bits(rng, (n, k), 0.02)
+        wv = oracle.bf16_to_f64(w, so=so)
+        js = sorted({0, 1, 7, 8, 63, 64, 127, 128, k // 2, k - 2, k - 1} & set(range(k)))
+        x = np.zeros((len(js), k), dtype=np.uint16)
+        for row, j in enumerate(js):
+            x[row, j] = 0x3F80
+        y, s = oracle.gemv(w, x, so=so)
+        for row, j in enumerate(js):
+            assert np.array_equal(y[row], wv[:, j]), f"one-hot {n}x{k} j={j}"
+            assert np.array_equal(s[row], np.abs(wv[:, j])), f"one-hot s_abs j={j}"
+
+
+def pin_constant_w(so):
+    """W = c = 2^-6 everywhere, x in {-2..2}: y = c * sum(x), exact at every partial sum."""
+    rng = np.random.default_rng(13)
+    ints = {-2: 0xC000, -1: 0xBF80, 0: 0x0000, 1: 0x3F80, 2: 0x4000}
+    for n, k, m in ((5, 129, 1), (33, 1000, 3), (16, 14337, 2)):
+        w = np.full((n, k), 0x3C80, dtype=np.uint16)
+        xi = rng.integers(-2, 3, size=(m, k))
+        x = np.vectorize(ints.get)(xi).astype(np.uint16)
+        y, s = oracle.gemv(w, x, so=so)
+        want = (2.0 ** -6) * xi.sum(axis=1)
+        want_abs = (2.0 ** -6) * np.abs(xi).sum(axis=1)
+        assert np.array_equal(y, np.repeat(want[:, None], n, axis=1)), f"const {n}x{k}"
+        assert np.array_equal(s, np.repeat(want_abs[:, None], n, axis=1)), "const s_abs"
+
+
+# --------------------------------------------------------------------------- brute force
+def pin_brute_force(so):
+    """Exact rational sums on tiny strided problems whose padding holds NaN bits."""
+    rng = np.random.default_rng(14)
+    for n in (1, 2, 3, 5, 12):
+        for k in (1, 2, 7, 8, 9, 63, 64, 65, 70):
+            for m in (1, 2, 3):
+                wide = (n + k + m) % 2 == 0
+                ldw, ldx = k + 3, k + 5
+                wbuf = np.full((n, ldw), 0x7FC0, dtype=np.uint16)   # NaN padding
+                xbuf = np.full((m, ldx), 0x7FC0, dtype=np.uint16)
+                wbuf[:, :k] = _rand_bits(rng, (n, k), 0.02, wide)
+                xbuf[:, :k] = _rand_bits(rng, (m, k), 1.0, wide)
+                y, s = oracle.gemv(wbuf, xbuf[:, :k], so=so)
+                assert y.shape == (m, n)
+                assert np.isfinite(y).all() and np.isfinite(s).all(), \
+                    f"non-finite output (padding read?) n={n} k={k} m={m}"
+                we = [_exact(wbuf[r, :k]) for r in range(n)]
+                xe = [_exact(xbuf[i, :k]) for i in range(m)]
+                for i in range(m):
+                    for r in range(n):
+                        terms = [a * b for a, b in zip(we[r], xe[i])]
+                        exact = sum(terms, Fraction(0))
+                        mag = sum((abs(t) for t in terms), Fraction(0))
+                        bound = gamma(k) * float(mag)
+                        assert abs(Fraction(y[i, r]) - exact) <= Fraction(bound), \
+                            f"brute force n={n} k={k} m={m} ({i},{r})"
+                        assert abs(Fraction(s[i, r]) - mag) <= Fraction(bound), \
+                            f"brute force s_abs n={n} k={k} m={m}"
+
+
+def pin_cancellation(so):
+    """Terms chosen to cancel: +a, -a pairs around one small survivor; exact answer known."""
+    rng = np.random.default_rng(15)
+    k = 257
+    big = _rand_bits(rng, (128,), 1.0, wide_exponents=True)
+    w = np.concatenate([big, big ^ np.uint16(0x8000), np.array([0x3C80], np.uint16)])[None, :]
+    x = np.full((1, k), 0x3F80, dtype=np.uint16)
+    y, s = oracle.gemv(w, x, so=so)
+    # every +a is added before its -a, so with exact products the fp64 result is within
+    # gamma_K * s_abs of the exact 2^-6
+    assert abs(y[0, 0] - 2.0 ** -6) <= gamma(k) * s[0, 0], "cancellation"
+
+
+# --------------------------------------------------------------------------- library
+def pin_numpy_matmul(so):
+    rng = np.random.default_rng(16)
+    for n, k, m in ((1024, 4096, 1), (7, 129, 1), (33, 1000, 1), (257, 14337, 3)):
+        w = _rand_bits(rng, (n, k), 0.02)
+        x = _rand_bits(rng, (m, k), 1.0)
+        y, s = oracle.gemv(w, x, nthreads=4, so=so)
+        wv = oracle.bf16_to_f64(w, so=so)
+        xv = oracle.bf16_to_f64(x, so=so)
+        ref = xv @ wv.T
+        ref_abs = np.abs(xv) @ np.abs(wv).T
+        tol = 2 * gamma(k) * ref_abs
+        assert np.all(np.abs(y - ref) <= tol), f"numpy matmul {n}x{k}x{m}"
+        assert np.all(np.abs(s - ref_abs) <= tol), f"numpy s_abs {n}x{k}x{m}"
+
+
+def pin_thread_invariance(so):
+    rng = np.random.default_rng(17)
+    w = _rand_bits(rng, (301, 777), 0.02)
+    x = _rand_bits(rng, (2, 777), 1.0)
+    y1, s1 = oracle.gemv(w, x, nthreads=1, so=so)
+    y4, s4 = oracle.gemv(w, x, nthreads=4, so=so)
+    assert np.array_equal(y1, y4) and np.array_equal(s1, s4), "thread count changes result"
+
+
+PINS = (pin_bf16_decode, pin_identity, pin_one_hot, pin_constant_w, pin_brute_force,
+        pin_cancellation, pin_numpy_matmul, pin_thread_invariance)
+
+
+def run_all(lib_path: str) -> int:
+    """Run every pin against the library at lib_path; exit status 0 only if all pass."""
+    import ctypes
+    so = oracle._bind(ctypes.CDLL(lib_path))
+    for pin in PINS:
+        try:
+            pin(so)
+        except AssertionError as e:
+            print(f"REJECTED by {pin.__name__}: {e}")
+            return 1
+    print("all pins pass")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(run_all(sys.argv[1]))

@@ -1,0 +1,116 @@
+"""Seeded synthetic inputs for the decode GEMV, shared by the tests and the bench.
+
+This module holds no arithmetic of the GEMV itself: it only names the workload shapes and
+draws seeded bf16 tensors. Both the HIP path and the CPU oracle receive exactly the tensors
+drawn here (the oracle always sees the bf16 bits copied back from wherever they were drawn),
+so the generator affects reproducibility only, never correctness.
+
+Shapes are the Llama 3.1 8B projection shapes the decode-GEMV page uses ("A strong answer",
+causes 1 and 3, and the split-K reversal paragraph on the LM head). Values are dense and
+unstructured: float32 normal samples scaled by sigma and rounded to bf16 (round to nearest
+even), W with sigma 0.02 and x with sigma 1.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+SIGMA_W = 0.02
+SIGMA_X = 1.0
+
+# Llama 3.1 8B projection shapes (rows N, reduction K).
+HIDDEN = 4096
+INTERMEDIATE = 14336
+Q_ROWS = 4096
+KV_ROWS = 1024
+VOCAB = 128256
+LAYERS = 32
+
+
+@dataclass(frozen=True)
+class Gemv:
+    """One GEMV problem: y[m] = W . x[m] with W [n, k] and X [m, k]."""
+    name: str
+    n: int
+    k: int
+    m: int = 1
+    segments: tuple[int, ...] = ()   # row split of a fused projection, sums to n
+
+    @property
+    def alg_bytes(self) -> int:
+        """Bytes a perfect kernel moves: W and X read once (bf16), Y written once (fp32)."""
+        return 2 * self.n * self.k + 2 * self.m * self.k + 4 * self.m * self.n
+
+
+@dataclass(frozen=True)
+class Config:
+    index: int
+    title: str
+    gemvs: tuple[Gemv, ...] = field(default_factory=tuple)
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+
+def decode_step_gemvs(layers: int = LAYERS) -> tuple[Gemv, ...]:
+    """The GEMV sequence of one batch-1 decode step, in stream order."""
+    seq = []
+    for layer in range(layers):
+        seq.append(Gemv(f"L{layer}.qkv", Q_ROWS + 2 * KV_ROWS, HIDDEN,
+                        segments=(Q_ROWS, KV_ROWS, KV_ROWS)))
+        seq.append(Gemv(f"L{layer}.o", HIDDEN, HIDDEN))
+        seq.append(Gemv(f"L{layer}.gate_up", 2 * INTERMEDIATE, HIDDEN,
+                        segments=(INTERMEDIATE, INTERMEDIATE)))
+        seq.append(Gemv(f"L{layer}.down", HIDDEN, INTERMEDIATE))
+    seq.append(Gemv("lm_head", VOCAB, HIDDEN))
+    return tuple(seq)
+
+
+CONFIGS: tuple[Config, ...] = (
+    Config(0, "k_proj GEMV 1024x4096 with tails 7x129 and 33x1000, batch 1",
+           (Gemv("k_proj", KV_ROWS, HIDDEN), Gemv("tail_7x129", 7, 129), Gemv("tail_33x1000", 33, 1000))),
+    Config(1, "split-K stress GEMV, down_proj 4096x14336, batch 1",
+           (Gemv("down", HIDDEN, INTERMEDIATE),)),
+    Config(2, "fused projections at batch 1: QKV 6144x4096 and gate_up 28672x4096",
+           (Gemv("qkv", Q_ROWS + 2 * KV_ROWS, HIDDEN, segments=(Q_ROWS, KV_ROWS, KV_ROWS)),
+            Gemv("gate_up", 2 * INTERMEDIATE, HIDDEN, segments=(INTERMEDIATE, INTERMEDIATE)))),
+    Config(3, "full batch-1 decode-step GEMV sequence (32 layers + lm_head) in one graph",
+           decode_step_gemvs()),
+    Config(4, "skinny-batch GEMV 4096x14336 at M in {1,2,4,8,16}, tail 4097x14337 at M=3",
+           tuple(Gemv(f"skinny_m{m}", HIDDEN, INTERMEDIATE, m) for m in (1, 2, 4, 8, 16))
+           + (Gemv("skinny_tail_m3", HIDDEN + 1, INTERMEDIATE + 1, 3),)),
+)
+
+
+def generator(seed: int, device: str | torch.device = "cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def bf16_normal(shape, sigma: float, gen: torch.Generator,
+                device: str | torch.device = "cpu") -> torch.Tensor:
+    """float32 N(0, 1) samples times sigma, rounded to bf16."""
+    t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return t.mul_(sigma).to(torch.bfloat16)
+
+
+def draw_gemv(g: Gemv, gen: torch.Generator, device: str | torch.device = "cpu"):
+    """Draw (W [n, k], X [m, k]) for one GEMV, W first, from the given generator."""
+    w = bf16_normal((g.n, g.k), SIGMA_W, gen, device)
+    x = bf16_normal((g.m, g.k), SIGMA_X, gen, device)
+    return w, x
+
+
+def draw_config(cfg: Config, device: str | torch.device = "cpu"):
+    """Draw every GEMV of a config in listed order from one generator seeded 1000 + index."""
+    gen = generator(cfg.seed, device)
+    return [draw_gemv(g, gen, device) for g in cfg.gemvs]
+
+
+def bf16_bits(t: torch.Tensor):
+    """The raw bf16 bit patterns of a tensor as a contiguous host uint16 numpy array."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view("uint16")
