@@ -1,0 +1,278 @@
+"""ctypes binding for libbbd_gemv.so: argument marshalling only.
+
+Every step of the GEMV runs in the library's HIP kernels. This module turns torch tensors
+into device pointers, leading dimensions and a stream handle, calls the C ABI declared in
+include/gemv.h and raises GemvError on any status other than GEMV_OK. There is no fallback:
+if the library is missing, importing the package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libbbd_gemv.so")
+
+MAX_M = 16
+MAX_SEGMENTS = 4
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    INVALID_ARG = 1
+    MISALIGNED = 2
+    WORKSPACE = 3
+    DEVICE = 4
+    CAPTURE = 5
+
+
+class GemvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = Status(status) if status in Status._value2member_map_ else status
+        hip = _lib.gemv_last_hip_error() if status in (Status.DEVICE, Status.CAPTURE) else 0
+        self.hip_error = hip
+        msg = _lib.gemv_status_string(int(status)).decode()
+        super().__init__(f"{where}: {msg} (status {int(status)}, hipError {hip})")
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("splits", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
+                ("waves_per_block", ctypes.c_int), ("unroll", ctypes.c_int)]
+
+
+class DeviceDesc(ctypes.Structure):
+    _fields_ = [("compute_units", ctypes.c_int), ("hbm_bytes_per_s", ctypes.c_double),
+                ("latency_s", ctypes.c_double)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("splits", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
+                ("waves_per_block", ctypes.c_int), ("unroll", ctypes.c_int),
+                ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int),
+                ("block_threads", ctypes.c_int), ("slice", ctypes.c_int64),
+                ("depth_bound", ctypes.c_int), ("bytes_in_flight_per_cu", ctypes.c_double),
+                ("bytes_in_flight_needed", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("n", ctypes.c_int64), ("ldw", ctypes.c_int64),
+                ("Y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+
+
+# Exported symbols and their C signatures (kept in the order of include/gemv.h).
+_I64, _P, _INT, _SZ = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "gemv_bytes_in_flight": (ctypes.c_double, [ctypes.c_double, ctypes.c_double]),
+    "gemv_plan": (_INT, [ctypes.POINTER(_P), _I64, _I64, _INT, _INT, ctypes.POINTER(PlanOpts)]),
+    "gemv_plan_for": (_INT, [ctypes.POINTER(_P), _I64, _I64, _INT, ctypes.POINTER(DeviceDesc),
+                             ctypes.POINTER(PlanOpts)]),
+    "gemv_workspace_size": (_SZ, [_P]),
+    "gemv_plan_query": (_INT, [_P, ctypes.POINTER(PlanInfo)]),
+    "gemv_plan_destroy": (None, [_P]),
+    "gemv_run": (_INT, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _SZ, _P]),
+    "gemv_fused_run": (_INT, [_P, ctypes.POINTER(Segment), _INT, _P, _I64, _P, _SZ, _P]),
+    "gemv_graph_begin": (_INT, [_P]),
+    "gemv_graph_end": (_INT, [_P, ctypes.POINTER(_P)]),
+    "gemv_graph_launch": (_INT, [_P, _P]),
+    "gemv_graph_destroy": (None, [_P]),
+    "gemv_status_string": (ctypes.c_char_p, [_INT]),
+    "gemv_last_hip_error": (_INT, []),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(the GEMV has no fallback path)")
+    so = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(so, name)
+        fn.restype = res
+        fn.argtypes = args
+    return so
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != Status.OK:
+        raise GemvError(status, where)
+
+
+def bytes_in_flight(bytes_per_s: float, latency_s: float) -> float:
+    return float(_lib.gemv_bytes_in_flight(bytes_per_s, latency_s))
+
+
+def _opts(splits, rows_per_wave, waves_per_block, unroll):
+    return PlanOpts(int(splits), int(rows_per_wave), int(waves_per_block), int(unroll))
+
+
+class Plan:
+    """An immutable launch plan for Y[M][N] = X[M][K] . W[N][K]^T.
+
+    With `desc` (compute_units, hbm_bytes_per_s, latency_s) the plan is made on the host
+    only, without touching a GPU; otherwise for the given CUDA/HIP device (default: current).
+    """
+
+    def __init__(self, n: int, k: int, m: int = 1, device=None, *, splits: int = 0,
+                 rows_per_wave: int = 0, waves_per_block: int = 0, unroll: int = 0,
+                 desc: tuple | None = None):
+        self._h = ctypes.c_void_p()
+        opts = _opts(splits, rows_per_wave, waves_per_block, unroll)
+        if desc is not None:
+            d = DeviceDesc(int(desc[0]), float(desc[1]), float(desc[2]))
+            st = _lib.gemv_plan_for(ctypes.byref(self._h), n, k, m, ctypes.byref(d),
+                                    ctypes.byref(opts))
+        else:
+            if device is None:
+                device = torch.cuda.current_device()
+            idx = torch.device(device).index if not isinstance(device, int) else device
+            st = _lib.gemv_plan(ctypes.byref(self._h), n, k, m, int(idx or 0),
+                                ctypes.byref(opts))
+        _check(st, "gemv_plan")
+        self.n, self.k, self.m = int(n), int(k), int(m)
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def workspace_size(self) -> int:
+        return int(_lib.gemv_workspace_size(self._h))
+
+    @property
+    def info(self) -> dict:
+        out = PlanInfo()
+        _check(_lib.gemv_plan_query(self._h, ctypes.byref(out)), "gemv_plan_query")
+        return out.as_dict()
+
+    def alloc_workspace(self, device=None) -> torch.Tensor | None:
+        """A zero-filled device buffer big enough for this plan (None if it needs none)."""
+        size = self.workspace_size
+        if size == 0:
+            return None
+        return torch.zeros(size, dtype=torch.uint8, device=device or "cuda")
+
+    def close(self):
+        if self._h:
+            _lib.gemv_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _row_stride(t: torch.Tensor, what: str) -> int:
+    if t.dim() == 1:
+        return t.shape[0]
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 1-D or 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{what} rows must be contiguous")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def run(plan: Plan, W: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
+        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X . W^T on the GPU (Y overwritten). W bf16 [n, >=k], X bf16 [m, k] or [k],
+    Y fp32 [m, n] or [n]. Returns Y."""
+    if W.dtype != torch.bfloat16 or X.dtype != torch.bfloat16 or Y.dtype != torch.float32:
+        raise TypeError("W and X must be bfloat16 and Y float32")
+    ws_ptr, ws_bytes = _ws(workspace)
+    st = _lib.gemv_run(plan.handle, W.data_ptr(), _row_stride(W, "W"), X.data_ptr(),
+                       _row_stride(X, "X"), Y.data_ptr(), _row_stride(Y, "Y"), ws_ptr,
+                       ws_bytes, _stream_handle(stream))
+    _check(st, "gemv_run")
+    return Y
+
+
+def fused_run(plan: Plan, segments, X: torch.Tensor, workspace: torch.Tensor | None = None,
+              stream=None):
+    """One launch over several (W_i, Y_i) pairs that share X (fused QKV / gate_up)."""
+    segs = list(segments)
+    arr = (Segment * max(len(segs), 1))()
+    for i, (w, y) in enumerate(segs):
+        if w.dtype != torch.bfloat16 or y.dtype != torch.float32:
+            raise TypeError("segment W must be bfloat16 and Y float32")
+        arr[i] = Segment(w.data_ptr(), w.shape[0], _row_stride(w, "W"), y.data_ptr(),
+                         _row_stride(y, "Y") if y.dim() == 2 else w.shape[0])
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    ws_ptr, ws_bytes = _ws(workspace)
+    st = _lib.gemv_fused_run(plan.handle, arr, len(segs), X.data_ptr(), _row_stride(X, "X"),
+                             ws_ptr, ws_bytes, _stream_handle(stream))
+    _check(st, "gemv_fused_run")
+
+
+class Graph:
+    """Capture gemv_run / gemv_fused_run calls issued on `stream` into one replayable graph.
+
+        with Graph(stream) as g:      # begin capture
+            run(...); fused_run(...)  # recorded, not executed
+        g.launch()                    # replay
+    """
+
+    def __init__(self, stream):
+        self.stream = stream
+        self._h = ctypes.c_void_p()
+
+    def begin(self):
+        _check(_lib.gemv_graph_begin(_stream_handle(self.stream)), "gemv_graph_begin")
+
+    def end(self):
+        _check(_lib.gemv_graph_end(_stream_handle(self.stream), ctypes.byref(self._h)),
+               "gemv_graph_end")
+
+    def __enter__(self):
+        self.begin()
+        return self
+
+    def __exit__(self, exc_type, exc, tb):
+        if exc_type is None:
+            self.end()
+        else:
+            try:
+                self.end()
+            finally:
+                self.destroy()
+
+    def launch(self, stream=None):
+        _check(_lib.gemv_graph_launch(self._h, _stream_handle(stream or self.stream)),
+               "gemv_graph_launch")
+
+    def destroy(self):
+        if self._h:
+            _lib.gemv_graph_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass

@@ -1,0 +1,679 @@
+// gemv.hip - gfx950 (CDNA4) kernels for the decode GEMV and the launching half of the C ABI.
+//
+// Y[m][n] = sum_k W[n][k] * X[m][k], W row-major bf16, X bf16, fp32 accumulation.
+//
+// Kernel design (decode-GEMV page, "Decode GEMV at half of HBM bandwidth", "A strong
+// answer"; GPU performance chains page, "A coalesced warp load"):
+//   - One 64-lane wave owns R output rows over one K slice. Lane l reads the 16-byte
+//     vectors l, l+64, l+128, ... of each row, so one wave-wide load instruction covers
+//     1 KiB of contiguous row bytes - the wave64 form of "lanes walk along K".
+//   - Each lane issues U x R independent 16-byte W loads (nontemporal: W is read once)
+//     before it consumes any, which is what keeps enough bytes in flight per CU for
+//     Little's law on HBM3E (cause 2 of the section above).
+//   - The multiply-add is v_dot2c_f32_bf16: two bf16 products summed into an fp32
+//     accumulator per instruction, with no widening step. One accumulator chain per
+//     (row, batch) per lane, in vector order, so the summation order depends only on the
+//     K slice - not on R, U or M.
+//   - A fixed DPP tree reduces the 64 lane partials (quad_perm, row_half_mirror,
+//     row_mirror, row_bcast:15, row_bcast:31), then lane 63 holds the row sum.
+//   - Split-K (cause 1): blockIdx.y selects the K slice. With more than one slice each
+//     wave writes its partial sums to the workspace (pass 1); the workgroup that arrives
+//     last for a row block - found with one ticket counter per row block - then adds the S
+//     partials of each of its outputs in slice order 0, 1, ..., S-1 (pass 2) and resets
+//     the counter. The order is fixed, so the result is bitwise reproducible; no atomic
+//     ever touches a sum (the page's follow-up on a result that differs in the last bit
+//     between runs). Doing pass 2 inside the same launch saves a kernel launch per GEMV,
+//     which on this GPU costs about as much as streaming 30 MB.
+// There is no LDS staging of W: a GEMV has no reuse of W (the page's common mistakes).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <array>
+#include <utility>
+
+#include "plan.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct Seg {
+    const uint16_t *w;  // row 0 of the segment's weight
+    int64_t ldw;
+    float *y;           // row 0 of the segment's output
+    int64_t ldy;
+    int32_t row0;       // first global row of the segment
+    int32_t pad;
+};
+
+struct Problem {
+    Seg seg[GEMV_MAX_SEGMENTS];
+    const uint16_t *x;
+    int64_t ldx;
+    float *partial;     // [S][M][N] when the plan splits K, else null
+    unsigned *tickets;  // [grid_x] arrival counters, zero between calls (split plans only)
+    int32_t nseg;
+    int32_t n;
+    int32_t k;
+    int32_t slice;
+};
+
+// ---------------------------------------------------------------------------- helpers
+
+// Element access goes through by-value scalars: clang mis-lowers __builtin_bit_cast
+// applied directly to an ext_vector element (it reads element 0).
+__device__ __forceinline__ float dot2(unsigned w, unsigned x, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, x), acc, false);
+}
+
+__device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc)
+{
+    unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+    unsigned x0 = x.x, x1 = x.y, x2 = x.z, x3 = x.w;
+    acc = dot2(w0, x0, acc);
+    acc = dot2(w1, x1, acc);
+    acc = dot2(w2, x2, acc);
+    acc = dot2(w3, x3, acc);
+    return acc;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b)
+{
+    return __uint_as_float((unsigned)b << 16);
+}
+
+__device__ __forceinline__ u32x4 load_stream(const uint16_t *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ u32x4 load_cached(const uint16_t *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp(float v)
+{
+    // Lanes outside ROW_MASK keep `old` = 0, so adding the result leaves them unchanged.
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK,
+                                                      0xF, false));
+}
+
+// Sum of the 64 lane values, valid in lane 63. Fixed tree, hence deterministic.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]: pairs
+    v += dpp<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]: quads
+    v += dpp<0x141, 0xF>(v);  // row_half_mirror: 8 lanes
+    v += dpp<0x140, 0xF>(v);  // row_mirror: 16 lanes (a full DPP row)
+    v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+__device__ __forceinline__ float lane63(float v)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Segment holding global row `row` (segments are in row order). Select chain, no
+// dynamic indexing, so it works for uniform and per-lane rows alike.
+struct RowRef {
+    const uint16_t *w;
+    float *y;
+    int64_t ldy;
+};
+
+__device__ __forceinline__ RowRef locate(const Problem &p, int row)
+{
+    const uint16_t *w = p.seg[0].w + (int64_t)row * p.seg[0].ldw;
+    float *y = p.seg[0].y + row;
+    int64_t ldy = p.seg[0].ldy;
+#pragma unroll
+    for (int i = 1; i < GEMV_MAX_SEGMENTS; ++i) {
+        if (i < p.nseg && row >= p.seg[i].row0) {
+            int local = row - p.seg[i].row0;
+            w = p.seg[i].w + (int64_t)local * p.seg[i].ldw;
+            y = p.seg[i].y + local;
+            ldy = p.seg[i].ldy;
+        }
+    }
+    return {w, y, ldy};
+}
+
+// Reduce R x M lane partials, then lane (r * M + m) stores output (row_first + r, m).
+template <int M, int R>
+__device__ __forceinline__ void finish(const Problem &p, float (&acc)[R][M], int row_first,
+                                       int split, int lane)
+{
+    float out = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float s = lane63(wave_sum(acc[r][m]));
+            if (lane == r * M + m)
+                out = s;
+        }
+    }
+    if (lane < R * M) {
+        int r = lane / M;
+        int m = lane - r * M;
+        int row = row_first + r;
+        if (row < p.n) {
+            if (p.partial) {
+                p.partial[((int64_t)split * M + m) * p.n + row] = out;
+            } else {
+                RowRef ref = locate(p, row);
+                ref.y[(int64_t)m * ref.ldy] = out;
+            }
+        }
+    }
+}
+
+// Pass 2 of split-K, run by the whole workgroup after its waves stored their partials.
+// The last of the S workgroups of row block blockIdx.x to arrive sums the partials of the
+// block's rows in slice order and leaves the ticket at zero for the next call.
+__device__ __forceinline__ void combine_if_last(const Problem &p, int m_count,
+                                                int rows_per_block)
+{
+    __shared__ unsigned s_last;
+    __threadfence();        // this wave's partial stores are complete and visible device-wide
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned ticket = __hip_atomic_fetch_add(p.tickets + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        s_last = ticket == gridDim.y - 1;
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    __threadfence();        // acquire: the other slices' partials are visible to this CU
+    const int row0 = blockIdx.x * rows_per_block;
+    const int rows = min(rows_per_block, p.n - row0);
+    const int64_t plane = (int64_t)m_count * p.n;   // one slice's partials
+    for (int t = threadIdx.x; t < rows * m_count; t += blockDim.x) {
+        const int m = t / rows;
+        const int row = row0 + (t - m * rows);
+        const float *src = p.partial + (int64_t)m * p.n + row;
+        float v = src[0];
+        for (unsigned sl = 1; sl < gridDim.y; ++sl)
+            v += src[sl * plane];
+        RowRef ref = locate(p, row);
+        ref.y[(int64_t)m * ref.ldy] = v;
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(p.tickets + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------- fast path
+// VGPRs a fast-path wave needs to hold every load of one unrolled step at once, plus
+// accumulators and addressing; the occupancy hint below lets the compiler use that many
+// instead of interleaving waits into the load burst to stay at 8 waves per SIMD.
+template <int M, int R, int U>
+constexpr int fast_vgprs()
+{
+    return 4 * U * (R + M) + R * M + 24;
+}
+
+template <int M, int R, int U>
+constexpr int fast_waves_per_simd()
+{
+    return 512 / fast_vgprs<M, R, U>() >= 8 ? 8 : 512 / fast_vgprs<M, R, U>();
+}
+
+// One wave's R rows over its K slice (split = blockIdx.y).
+template <int M, int R, int U>
+__device__ __forceinline__ void fast_rows(const Problem &p, int row_first, int lane)
+{
+    const int split = blockIdx.y;
+    const int k0 = split * p.slice;
+    const int len = min(p.k - k0, p.slice);
+    const int nvec = len >> 3;
+    const int rem = len & 7;
+    const int full = nvec >> 6;   // steps in which every lane has a vector
+
+    const uint16_t *wrow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        // Rows past N (last wave of the grid) re-read row N-1; their sums are discarded.
+        int row = min(row_first + r, p.n - 1);
+        wrow[r] = locate(p, row).w + k0;
+    }
+    const uint16_t *xk = p.x + k0;
+
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            acc[r][m] = 0.f;
+
+    int step = 0;
+    for (; step + U <= full; step += U) {
+        u32x4 wv[U][R];
+        u32x4 xv[U][M];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                wv[u][r] = load_stream(wrow[r] + 8 * (lane + 64 * (step + u)));
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                xv[u][m] = load_cached(xk + m * p.ldx + 8 * (lane + 64 * (step + u)));
+        // Keep the whole burst of loads ahead of the first use: without this the
+        // scheduler interleaves waits into it to save registers, cutting loads in flight.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    acc[r][m] = dot8(wv[u][r], xv[u][m], acc[r][m]);
+    }
+    for (; step < full; ++step) {
+        u32x4 wv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            wv[r] = load_stream(wrow[r] + 8 * (lane + 64 * step));
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            u32x4 xv = load_cached(xk + m * p.ldx + 8 * (lane + 64 * step));
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[r][m] = dot8(wv[r], xv, acc[r][m]);
+        }
+    }
+    // Last, partial wave step: only lanes whose vector lies inside the slice.
+    const int v_last = lane + 64 * full;
+    if (v_last < nvec) {
+        u32x4 wv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            wv[r] = load_stream(wrow[r] + 8 * v_last);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            u32x4 xv = load_cached(xk + m * p.ldx + 8 * v_last);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[r][m] = dot8(wv[r], xv, acc[r][m]);
+        }
+    }
+    // Ragged tail of fewer than 8 elements (only the final slice can have one).
+    if (lane < rem) {
+        const int kk = 8 * nvec + lane;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float w = bf16_to_f32(wrow[r][kk]);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                acc[r][m] = fmaf(w, bf16_to_f32(xk[m * p.ldx + kk]), acc[r][m]);
+        }
+    }
+    finish<M, R>(p, acc, row_first, split, lane);
+}
+
+// W and X 16-byte aligned with leading dimensions that are multiples of 8. Waves whose
+// rows lie past N skip the row work but still take part in the split-K combine.
+template <int M, int R, int U>
+__global__ void __launch_bounds__(512)
+    __attribute__((amdgpu_waves_per_eu(1, fast_waves_per_simd<M, R, U>()))) gemv_fast(Problem p)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int waves = blockDim.x >> 6;
+    const int row_first = (blockIdx.x * waves + wave) * R;
+    if (row_first < p.n)
+        fast_rows<M, R, U>(p, row_first, lane);
+    if (p.partial)
+        combine_if_last(p, M, waves * R);
+}
+
+// ---------------------------------------------------------------------------- unaligned
+// Any 2-byte-aligned layout. Per row, the 16-byte vectors are placed where the row's W
+// address is 16-byte aligned (starting at element h, 0 <= h < 8); the up to 7 elements
+// before the first vector and after the last one are scalar. The matching x window sits
+// at a shift q (per row and batch) from X's own 16-byte grid; it is built from the two
+// aligned x vectors around it, or element by element near the ends of a row of X.
+
+// Elements q .. q+7 of the 16-element concatenation a|b (wave-uniform q in 0..7).
+__device__ __forceinline__ u32x4 funnel(u32x4 a, u32x4 b, int q)
+{
+    unsigned d0 = a.x, d1 = a.y, d2 = a.z, d3 = a.w;
+    unsigned d4 = b.x, d5 = b.y, d6 = b.z, d7 = b.w;
+    unsigned s0, s1, s2, s3, s4;
+    switch (q >> 1) {
+    case 0: s0 = d0; s1 = d1; s2 = d2; s3 = d3; s4 = d4; break;
+    case 1: s0 = d1; s1 = d2; s2 = d3; s3 = d4; s4 = d5; break;
+    case 2: s0 = d2; s1 = d3; s2 = d4; s3 = d5; s4 = d6; break;
+    default: s0 = d3; s1 = d4; s2 = d5; s3 = d6; s4 = d7; break;
+    }
+    const unsigned sh = (unsigned)(q & 1) * 2u;   // bytes
+    u32x4 r;
+    r.x = __builtin_amdgcn_alignbyte(s1, s0, sh);
+    r.y = __builtin_amdgcn_alignbyte(s2, s1, sh);
+    r.z = __builtin_amdgcn_alignbyte(s3, s2, sh);
+    r.w = __builtin_amdgcn_alignbyte(s4, s3, sh);
+    return r;
+}
+
+// x[k .. k+7] of one row of X with k + 8 <= K; q = element offset of x + k from the
+// 16-byte grid.
+__device__ __forceinline__ u32x4 x_window(const uint16_t *xr, int k, int K, int q)
+{
+    if (k >= 8 && k + 16 <= K) {
+        const uint16_t *base = xr + (k - q);   // 16-byte aligned, inside the row
+        return funnel(load_cached(base), load_cached(base + 8), q);
+    }
+    u32x4 r;
+    r.x = (unsigned)xr[k + 0] | ((unsigned)xr[k + 1] << 16);
+    r.y = (unsigned)xr[k + 2] | ((unsigned)xr[k + 3] << 16);
+    r.z = (unsigned)xr[k + 4] | ((unsigned)xr[k + 5] << 16);
+    r.w = (unsigned)xr[k + 6] | ((unsigned)xr[k + 7] << 16);
+    return r;
+}
+
+template <int M>
+__global__ void __launch_bounds__(512) gemv_unaligned(Problem p, int rows_per_wave)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int waves = blockDim.x >> 6;
+    const int row_first = (blockIdx.x * waves + wave) * rows_per_wave;
+    const int split = blockIdx.y;
+    const int k0 = split * p.slice;
+    const int kend = min(p.k, k0 + p.slice);
+
+    for (int r = 0; r < rows_per_wave; ++r) {
+        const int row = row_first + r;
+        if (row >= p.n)
+            break;
+        const uint16_t *wr = locate(p, row).w;
+        const int h = (int)((8u - (unsigned)(((uintptr_t)wr >> 1) & 7u)) & 7u);
+        const int ka = k0 + h;                        // first vector start (k0 % 8 == 0)
+        const int nvec = ka + 8 <= kend ? (kend - ka) >> 3 : 0;
+        const int head_end = min(ka, kend);
+        const int tail_begin = max(head_end, ka + 8 * nvec);
+
+        int q[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            q[m] = (int)((((uintptr_t)(p.x + m * p.ldx) >> 1) + (unsigned)h) & 7u);
+
+        float acc[1][M];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            acc[0][m] = 0.f;
+
+        for (int v = lane; v < nvec; v += 64) {
+            const int kk = ka + 8 * v;
+            u32x4 wv = load_stream(wr + kk);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                acc[0][m] = dot8(wv, x_window(p.x + m * p.ldx, kk, p.k, q[m]), acc[0][m]);
+        }
+        // Lanes 0..7 take the head elements, lanes 8..15 the tail elements.
+        const int kk = lane < 8 ? k0 + lane : tail_begin + (lane - 8);
+        const bool take = lane < 8 ? kk < head_end : (lane < 16 && kk < kend);
+        if (take) {
+            float w = bf16_to_f32(wr[kk]);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                acc[0][m] = fmaf(w, bf16_to_f32(p.x[m * p.ldx + kk]), acc[0][m]);
+        }
+        finish<M, 1>(p, acc, row, split, lane);
+    }
+    if (p.partial)
+        combine_if_last(p, M, waves * rows_per_wave);
+}
+
+// ---------------------------------------------------------------------------- dispatch
+using FastKernel = void (*)(Problem);
+using UnalignedKernel = void (*)(Problem, int);
+
+template <size_t I>
+constexpr FastKernel fast_at()
+{
+    constexpr bbd::Variant v = bbd::kVariants[I];
+    return &gemv_fast<v.m, v.r, v.u>;
+}
+
+template <size_t... I>
+constexpr std::array<FastKernel, sizeof...(I)> fast_table(std::index_sequence<I...>)
+{
+    return {fast_at<I>()...};
+}
+
+constexpr size_t kNumVariants = sizeof(bbd::kVariants) / sizeof(bbd::kVariants[0]);
+const std::array<FastKernel, kNumVariants> kFast = fast_table(std::make_index_sequence<kNumVariants>{});
+
+template <size_t... I>
+constexpr std::array<UnalignedKernel, sizeof...(I)> unaligned_table(std::index_sequence<I...>)
+{
+    return {&gemv_unaligned<(int)I + 1>...};
+}
+
+const std::array<UnalignedKernel, GEMV_MAX_M> kUnaligned =
+    unaligned_table(std::make_index_sequence<GEMV_MAX_M>{});
+
+FastKernel find_fast(int m, int r, int u)
+{
+    for (size_t i = 0; i < kNumVariants; ++i)
+        if (bbd::kVariants[i].m == m && bbd::kVariants[i].r == r && bbd::kVariants[i].u == u)
+            return kFast[i];
+    return nullptr;
+}
+
+thread_local int g_last_hip_error = 0;
+
+gemv_status device_error(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return GEMV_ERR_DEVICE;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+bool aligned2(const void *p) { return ((uintptr_t)p & 1u) == 0; }
+
+// Validation shared by gemv_run and gemv_fused_run; makes no HIP call.
+gemv_status validate(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
+                     int64_t ldx, void *ws, size_t ws_bytes)
+{
+    if (!p || !segs || nseg < 1 || nseg > GEMV_MAX_SEGMENTS || !X)
+        return GEMV_ERR_INVALID_ARG;
+    if (p->m > 1 && ldx < p->k)
+        return GEMV_ERR_INVALID_ARG;
+    int64_t rows = 0;
+    for (int i = 0; i < nseg; ++i) {
+        const gemv_segment &s = segs[i];
+        if (!s.W || !s.Y || s.n < 1 || s.ldw < p->k || s.ldy < s.n)
+            return GEMV_ERR_INVALID_ARG;
+        rows += s.n;
+    }
+    if (rows != p->n)
+        return GEMV_ERR_INVALID_ARG;
+    if (!aligned2(X))
+        return GEMV_ERR_MISALIGNED;
+    for (int i = 0; i < nseg; ++i)
+        if (!aligned2(segs[i].W) || !aligned4(segs[i].Y))
+            return GEMV_ERR_MISALIGNED;
+    if (p->workspace) {
+        if (!ws || ws_bytes < p->workspace)
+            return GEMV_ERR_WORKSPACE;
+        if (!aligned4(ws))
+            return GEMV_ERR_MISALIGNED;
+    }
+    return GEMV_OK;
+}
+
+gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
+                   int64_t ldx, void *ws, size_t ws_bytes, void *stream)
+{
+    gemv_status st = validate(p, segs, nseg, X, ldx, ws, ws_bytes);
+    if (st != GEMV_OK)
+        return st;
+
+    Problem prob = {};
+    bool fast = aligned16(X) && (p->m == 1 || ldx % 8 == 0);
+    int64_t row0 = 0;
+    for (int i = 0; i < nseg; ++i) {
+        prob.seg[i].w = static_cast<const uint16_t *>(segs[i].W);
+        prob.seg[i].ldw = segs[i].ldw;
+        prob.seg[i].y = segs[i].Y;
+        prob.seg[i].ldy = segs[i].ldy;
+        prob.seg[i].row0 = (int32_t)row0;
+        row0 += segs[i].n;
+        fast = fast && aligned16(segs[i].W) && segs[i].ldw % 8 == 0;
+    }
+    prob.nseg = nseg;
+    prob.x = static_cast<const uint16_t *>(X);
+    prob.ldx = p->m > 1 ? ldx : 0;
+    prob.tickets = p->splits > 1 ? static_cast<unsigned *>(ws) : nullptr;
+    prob.partial = p->splits > 1
+                       ? reinterpret_cast<float *>(static_cast<char *>(ws) + p->partial_offset)
+                       : nullptr;
+    prob.n = (int32_t)p->n;
+    prob.k = (int32_t)p->k;
+    prob.slice = (int32_t)p->slice;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    dim3 grid((unsigned)p->grid_x, (unsigned)p->grid_y);
+    dim3 block((unsigned)p->block_threads);
+    hipError_t e;
+    if (fast) {
+        FastKernel k = find_fast(p->m, p->rows_per_wave, p->unroll);
+        if (!k)
+            return GEMV_ERR_INVALID_ARG;
+        void *args[] = {&prob};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, 0, s);
+    } else {
+        int r = p->rows_per_wave;
+        void *args[] = {&prob, &r};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(kUnaligned[p->m - 1]), grid, block,
+                            args, 0, s);
+    }
+    if (e != hipSuccess)
+        return device_error(e);
+    return GEMV_OK;
+}
+
+}  // namespace
+
+struct gemv_graph_s {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+extern "C" gemv_status gemv_plan(gemv_plan_t *out, int64_t n, int64_t k, int m, int device,
+                                 const gemv_plan_opts *opts)
+{
+    if (!out)
+        return GEMV_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (n < 1 || k < 1 || m < 1 || m > GEMV_MAX_M || device < 0)
+        return GEMV_ERR_INVALID_ARG;
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess)
+        return device_error(e);
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+        g_last_hip_error = 0;
+        return GEMV_ERR_DEVICE;
+    }
+    // MI355X: 8.0 TB/s HBM3E (published peak); the plan uses it only to report Little's law.
+    gemv_device_desc dev = {prop.multiProcessorCount, 8.0e12, bbd::kDefaultLatency};
+    gemv_status st = gemv_plan_for(out, n, k, m, &dev, opts);
+    if (st == GEMV_OK)
+        (*out)->device = device;
+    return st;
+}
+
+extern "C" gemv_status gemv_run(gemv_plan_t p, const void *W, int64_t ldw, const void *X,
+                                int64_t ldx, float *Y, int64_t ldy, void *workspace,
+                                size_t ws_bytes, void *stream)
+{
+    if (!p)
+        return GEMV_ERR_INVALID_ARG;
+    gemv_segment seg = {W, p->n, ldw, Y, ldy};
+    return launch(p, &seg, 1, X, ldx, workspace, ws_bytes, stream);
+}
+
+extern "C" gemv_status gemv_fused_run(gemv_plan_t p, const gemv_segment *segs, int nseg,
+                                      const void *X, int64_t ldx, void *workspace,
+                                      size_t ws_bytes, void *stream)
+{
+    return launch(p, segs, nseg, X, ldx, workspace, ws_bytes, stream);
+}
+
+extern "C" gemv_status gemv_graph_begin(void *stream)
+{
+    if (!stream)
+        return GEMV_ERR_CAPTURE;
+    hipError_t e = hipStreamBeginCapture(static_cast<hipStream_t>(stream),
+                                         hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return GEMV_ERR_CAPTURE;
+    }
+    return GEMV_OK;
+}
+
+extern "C" gemv_status gemv_graph_end(void *stream, gemv_graph_t *out)
+{
+    if (!out)
+        return GEMV_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!stream)
+        return GEMV_ERR_CAPTURE;
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamEndCapture(static_cast<hipStream_t>(stream), &graph);
+    if (e != hipSuccess || !graph) {
+        g_last_hip_error = (int)e;
+        return GEMV_ERR_CAPTURE;
+    }
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        return device_error(e);
+    }
+    gemv_graph_s *g = new (std::nothrow) gemv_graph_s{graph, exec};
+    if (!g) {
+        (void)hipGraphExecDestroy(exec);
+        (void)hipGraphDestroy(graph);
+        return GEMV_ERR_INVALID_ARG;
+    }
+    *out = g;
+    return GEMV_OK;
+}
+
+extern "C" gemv_status gemv_graph_launch(gemv_graph_t g, void *stream)
+{
+    if (!g)
+        return GEMV_ERR_INVALID_ARG;
+    hipError_t e = hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return device_error(e);
+    return GEMV_OK;
+}
+
+extern "C" void gemv_graph_destroy(gemv_graph_t g)
+{
+    if (!g)
+        return;
+    (void)hipGraphExecDestroy(g->exec);
+    (void)hipGraphDestroy(g->graph);
+    delete g;
+}
+
+extern "C" int gemv_last_hip_error(void) { return g_last_hip_error; }

@@ -1,0 +1,225 @@
+// plan.cpp - host-only planning for the decode GEMV: split count, tile, unroll, grid,
+// workspace and the summation-depth bound. Pure integer/float arithmetic, no HIP calls.
+//
+// The rule follows the decode-GEMV page ("Decode GEMV at half of HBM bandwidth",
+// "A strong answer"):
+//   - cause 1: a skinny output gives too few workgroups to cover the machine, so the
+//     reduction dimension is split as well until every CU has several workgroups;
+//   - the reversal paragraph: a shape whose row blocks alone already cover the machine
+//     several times (the LM head, gate_up) gets no split, because split-K costs extra
+//     partial-sum traffic and a second pass; the split count is chosen per shape;
+//   - cause 2 / Little's law: each lane keeps U independent 16-byte loads outstanding per
+//     row, and the plan reports the bytes that puts in flight per CU next to what
+//     bandwidth x latency demands.
+// The wave quantization chain of the GPU performance chains page is why the target is a
+// whole number of workgroups per CU rather than "just over one wave".
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "plan.h"
+
+namespace bbd {
+
+bool variant_supported(int m, int r, int u)
+{
+    for (const Variant &v : kVariants)
+        if (v.m == m && v.r == r && v.u == u)
+            return true;
+    return false;
+}
+
+}  // namespace bbd
+
+using namespace bbd;
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Defaults per batch size: (rows per wave, unroll). Larger M spends VGPRs on X vectors
+// and accumulators, so the W unroll shrinks.
+void default_tile(int m, int *r, int *u)
+{
+    if (m == 1) {
+        *r = 2;
+        *u = 4;
+    } else if (m <= 4) {
+        *r = 2;
+        *u = 4;
+    } else {
+        *r = 2;
+        *u = 2;
+    }
+}
+
+constexpr int kDefaultWaves = 4;
+
+// K elements per split for S splits: wave-step aligned when a slice spans more than one
+// wave-wide step, so every lane of every slice but the last walks the same vectors.
+int64_t slice_for(int64_t k, int s)
+{
+    int64_t per = ceil_div(k, s);
+    return per > kWaveStep ? round_up(per, kWaveStep) : round_up(per, kVecElems);
+}
+
+// The most fp32 roundings any product passes through: 4 chained dot2 steps per 16-byte
+// vector a lane accumulates (+1 inside the first dot2), 1 for a scalar head and 1 for a
+// scalar tail element, 6 levels of the wave64 reduction tree, and S-1 combine additions.
+int depth_for(int64_t slice, int s)
+{
+    int64_t vecs = ceil_div(slice, kVecElems);
+    int64_t per_lane = ceil_div(vecs, kWaveLanes);
+    return (int)(4 * per_lane + 1 + 2 + 6 + (s - 1));
+}
+
+bool valid_waves(int w) { return w == 1 || w == 2 || w == 4 || w == 8; }
+
+}  // namespace
+
+extern "C" double gemv_bytes_in_flight(double bytes_per_s, double latency_s)
+{
+    return bytes_per_s * latency_s;
+}
+
+extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int m,
+                                     const gemv_device_desc *dev, const gemv_plan_opts *opts)
+{
+    if (!out)
+        return GEMV_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!dev || dev->compute_units < 1 || !(dev->hbm_bytes_per_s > 0) || !(dev->latency_s > 0))
+        return GEMV_ERR_INVALID_ARG;
+    if (n < 1 || k < 1 || m < 1 || m > GEMV_MAX_M)
+        return GEMV_ERR_INVALID_ARG;
+    // Row indices and grid sizes are held in 32 bits on the device.
+    if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30)
+        return GEMV_ERR_INVALID_ARG;
+    gemv_plan_opts o = {0, 0, 0, 0};
+    if (opts)
+        o = *opts;
+    if (o.splits < 0 || o.rows_per_wave < 0 || o.waves_per_block < 0 || o.unroll < 0)
+        return GEMV_ERR_INVALID_ARG;
+
+    int r, u;
+    default_tile(m, &r, &u);
+    if (o.rows_per_wave)
+        r = o.rows_per_wave;
+    if (o.unroll)
+        u = o.unroll;
+    int waves = o.waves_per_block ? o.waves_per_block : kDefaultWaves;
+    if (!valid_waves(waves) || !variant_supported(m, r, u))
+        return GEMV_ERR_INVALID_ARG;
+
+    // The split count depends on N, K and the machine only - not on M - so that every
+    // row of a batched result is summed in the same order as the batch-1 result.
+    int r1, u1;
+    default_tile(1, &r1, &u1);
+    int64_t rows_per_block_s = (int64_t)(o.rows_per_wave ? r : r1) * waves;
+    int64_t row_blocks_s = ceil_div(n, rows_per_block_s);
+
+    int s;
+    int64_t slice;
+    if (o.splits) {
+        s = o.splits;
+        if (s > kMaxSplits)
+            return GEMV_ERR_INVALID_ARG;
+        slice = slice_for(k, s);
+        if (ceil_div(k, slice) != s)   // some slice would be empty
+            return GEMV_ERR_INVALID_ARG;
+    } else {
+        int64_t target = (int64_t)kTargetBlocksPerCU * dev->compute_units;
+        int64_t want = row_blocks_s >= target ? 1 : ceil_div(target, row_blocks_s);
+        int64_t cap = k / kMinSlice > 1 ? k / kMinSlice : 1;
+        if (want > cap)
+            want = cap;
+        if (want > kMaxSplits)
+            want = kMaxSplits;
+        s = (int)want;
+        slice = slice_for(k, s);
+        s = (int)ceil_div(k, slice);
+        // Split further if one slice would exceed the summation-depth bound.
+        while (depth_for(slice, s) > kMaxDepth && s < kMaxSplits) {
+            ++s;
+            slice = slice_for(k, s);
+            s = (int)ceil_div(k, slice);
+        }
+        // K beyond ~720k elements cannot meet the bound with 64 slices: refuse rather than
+        // return a plan whose result may miss the tolerance.
+        if (depth_for(slice, s) > kMaxDepth)
+            return GEMV_ERR_INVALID_ARG;
+    }
+
+    gemv_plan_s *p = new (std::nothrow) gemv_plan_s;
+    if (!p)
+        return GEMV_ERR_INVALID_ARG;
+    memset(p, 0, sizeof *p);
+    p->n = n;
+    p->k = k;
+    p->m = m;
+    p->device = -1;
+    p->dev = *dev;
+    p->splits = s;
+    p->rows_per_wave = r;
+    p->waves_per_block = waves;
+    p->unroll = u;
+    p->slice = slice;
+    p->grid_x = (int)ceil_div(n, (int64_t)r * waves);
+    p->grid_y = s;
+    p->block_threads = kWaveLanes * waves;
+    p->depth_bound = depth_for(slice, s);
+    if (s > 1) {
+        // One arrival ticket per row block (in a fixed-size region), then S x M x N fp32
+        // partial sums.
+        int64_t slots = p->grid_x > kTicketSlots ? p->grid_x : kTicketSlots;
+        p->partial_offset = (size_t)round_up(slots * (int64_t)sizeof(unsigned), 256);
+        p->workspace = p->partial_offset + (size_t)s * (size_t)m * (size_t)n * sizeof(float);
+    }
+
+    int64_t total_waves = (int64_t)p->grid_x * p->grid_y * waves;
+    int64_t per_cu = ceil_div(total_waves, dev->compute_units);
+    if (per_cu > kMaxWavesPerCU)
+        per_cu = kMaxWavesPerCU;
+    p->bif_per_cu = (double)per_cu * u * r * kWaveLanes * 16.0;
+    p->bif_needed = gemv_bytes_in_flight(dev->hbm_bytes_per_s, dev->latency_s) / dev->compute_units;
+    *out = p;
+    return GEMV_OK;
+}
+
+extern "C" size_t gemv_workspace_size(gemv_plan_t p) { return p ? p->workspace : 0; }
+
+extern "C" gemv_status gemv_plan_query(gemv_plan_t p, gemv_plan_info *info)
+{
+    if (!p || !info)
+        return GEMV_ERR_INVALID_ARG;
+    info->splits = p->splits;
+    info->rows_per_wave = p->rows_per_wave;
+    info->waves_per_block = p->waves_per_block;
+    info->unroll = p->unroll;
+    info->grid_x = p->grid_x;
+    info->grid_y = p->grid_y;
+    info->block_threads = p->block_threads;
+    info->slice = p->slice;
+    info->depth_bound = p->depth_bound;
+    info->bytes_in_flight_per_cu = p->bif_per_cu;
+    info->bytes_in_flight_needed = p->bif_needed;
+    return GEMV_OK;
+}
+
+extern "C" void gemv_plan_destroy(gemv_plan_t p) { delete p; }
+
+extern "C" const char *gemv_status_string(gemv_status s)
+{
+    switch (s) {
+    case GEMV_OK: return "ok";
+    case GEMV_ERR_INVALID_ARG: return "invalid argument";
+    case GEMV_ERR_MISALIGNED: return "misaligned pointer";
+    case GEMV_ERR_WORKSPACE: return "workspace missing or too small";
+    case GEMV_ERR_DEVICE: return "device error or unsupported device";
+    case GEMV_ERR_CAPTURE: return "graph capture error";
+    }
+    return "unknown status";
+}

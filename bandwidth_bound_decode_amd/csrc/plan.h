@@ -1,0 +1,68 @@
+// plan.h - internal: the plan object and the table of compiled kernel variants.
+//
+// Shared by plan.cpp (host arithmetic only, no HIP headers) and gemv.hip (launches).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gemv.h"
+
+namespace bbd {
+
+// Architectural facts the plan sizes launches for (CDNA4 / gfx950).
+constexpr int kWaveLanes = 64;          // lanes per wavefront
+constexpr int kVecElems = 8;            // bf16 elements per 16-byte load
+constexpr int kWaveStep = kWaveLanes * kVecElems;   // K elements one wave-wide load covers
+constexpr int kMaxWavesPerCU = 32;      // 4 SIMDs x 8 waves
+constexpr int kMaxSplits = 64;
+
+// Planning constants (tunable, see the plan rule in plan.cpp).
+constexpr int kTargetBlocksPerCU = 4;   // "several waves" of workgroups on every CU
+constexpr int64_t kMinSlice = 1024;     // never split K finer than this many elements
+constexpr int kMaxDepth = 160;          // gamma_160 (u = 2^-24) = 9.54e-6 < 1e-5
+constexpr double kDefaultLatency = 1.0e-6;   // assumed loaded HBM latency on MI355X
+// Ticket counters sit at the start of a split plan's workspace in a region of at least this
+// many slots, so that plans with up to this many row blocks can share one workspace in any
+// order without one plan's partial sums landing on another plan's tickets.
+constexpr int64_t kTicketSlots = 4096;
+
+// One compiled (M, R, U) combination of the aligned fast-path kernel. The unaligned path
+// exists for every M and takes R at run time.
+struct Variant {
+    int m, r, u;
+};
+
+// The fast-path kernels gemv.hip instantiates. Keep in sync with its dispatch table.
+constexpr Variant kVariants[] = {
+    {1, 1, 2}, {1, 1, 4}, {1, 1, 8}, {1, 2, 2}, {1, 2, 4}, {1, 2, 8}, {1, 4, 2}, {1, 4, 4},
+    {1, 4, 8},
+    {2, 1, 2}, {2, 1, 4}, {2, 2, 2}, {2, 2, 4},
+    {3, 1, 2}, {3, 1, 4}, {3, 2, 2}, {3, 2, 4},
+    {4, 1, 2}, {4, 1, 4}, {4, 2, 2}, {4, 2, 4},
+    {5, 1, 2}, {5, 2, 2}, {6, 1, 2}, {6, 2, 2}, {7, 1, 2}, {7, 2, 2}, {8, 1, 2}, {8, 2, 2},
+    {9, 1, 2}, {9, 2, 2}, {10, 1, 2}, {10, 2, 2}, {11, 1, 2}, {11, 2, 2}, {12, 1, 2},
+    {12, 2, 2}, {13, 1, 2}, {13, 2, 2}, {14, 1, 2}, {14, 2, 2}, {15, 1, 2}, {15, 2, 2},
+    {16, 1, 2}, {16, 2, 2},
+};
+
+bool variant_supported(int m, int r, int u);
+
+}  // namespace bbd
+
+struct gemv_plan_s {
+    int64_t n, k;
+    int m;
+    int device;                 // HIP device id, or -1 for a plan made by gemv_plan_for
+    gemv_device_desc dev;
+    int splits;                 // S
+    int rows_per_wave;          // R
+    int waves_per_block;
+    int unroll;                 // U
+    int64_t slice;              // K elements per split (multiple of 8)
+    int grid_x, grid_y, block_threads;
+    int depth_bound;
+    size_t workspace;           // ticket counters, then the split partials
+    size_t partial_offset;      // byte offset of the partial sums in the workspace
+    double bif_per_cu, bif_needed;
+};

@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Bench of the MI355X decode GEMV: achieved HBM TB/s and fraction of peak at Llama-8B shapes.
+
+Headline ("step" = one full GEMV pass): the down_proj GEMV, W 4096 x 14336 bf16, x bf16, fp32
+outputs, batch 1. Inputs are seeded synthetic tensors already resident in HBM. Each step uses
+the next of >= 1 GB of distinct weight copies, so no step is served from the 256 MB Infinity
+Cache or the 32 MB of L2 (the decode-GEMV page warns about matrices small enough to sit in
+cache, "Common mistakes"). Every launch in the timed region is bracketed by HIP events on the
+stream it runs on; throughput is whole-region bytes / whole-region time, and the roofline's
+`achieved` is algorithmic bytes / mean launch duration.
+
+Also reported on the same JSON line: the graph-replayed decode step (32 layers x [QKV,
+o_proj, gate_up, down] + lm_head), per-GEMV numbers for the other workload shapes, the
+oracle timed on the host cores, and the pages' H100 context.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM = 8.0e12                 # MI355X HBM3E, published peak, B/s
+METRIC = "achieved HBM TB/s and % of peak, bf16 GEMV batch 1 at Llama-8B shapes"
+ROTATION_BYTES = 1.0e9            # >= 1 GB of distinct weights per rotation arena
+COUNTERS_FILE = os.path.join(HERE, "profiles", "counters_down_4096x14336.json")
+KERNEL_SOURCES = [os.path.join(HERE, "bandwidth_bound_decode_amd", "csrc", f)
+                  for f in ("gemv.hip", "plan.cpp", "plan.h")]
+
+# The pages' H100 SXM context (decode-GEMV page and GPU performance chains page).
+H100 = {"hbm_TBps": 3.35, "sms": 132, "k_proj_transfer_us_at_peak": 2.5,
+        "goal_fraction_of_peak": 0.80}
+
+
+# ---------------------------------------------------------------------------- arithmetic
+def alg_bytes(n: int, k: int, m: int = 1) -> int:
+    """Bytes a perfect GEMV moves: W and X read once in bf16, Y written once in fp32."""
+    return 2 * n * k + 2 * m * k + 4 * m * n
+
+
+def seconds_at(nbytes: float, bytes_per_s: float) -> float:
+    return nbytes / bytes_per_s
+
+
+def mbu(nbytes: float, seconds: float, bytes_per_s: float) -> float:
+    """Memory-bandwidth utilisation: bytes moved per second over the peak."""
+    return nbytes / seconds / bytes_per_s
+
+
+def waves(programs: int, units: int) -> int:
+    return math.ceil(programs / units)
+
+
+def wave_efficiency(programs: int, units: int) -> float:
+    return programs / (waves(programs, units) * units)
+
+
+def ridge(flops_per_s: float, bytes_per_s: float) -> float:
+    return flops_per_s / bytes_per_s
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(launch_bytes_expected: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if there is
+    none or the kernels changed since it was taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if c.get("kernel_source_sha256") != kernel_source_hash():
+        return None, "kernel sources changed since the counters were taken"
+    fetch = c["fetch_kib_per_launch"] * 1024 * c["fetch_scale"]
+    write = c["write_kib_per_launch"] * 1024 * c["write_scale"]
+    return fetch + write, f"rocprofv3 FETCH_SIZE+WRITE_SIZE scaled by copy calibration"
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def pct(xs, q):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
+    return xs[i]
+
+
+# ---------------------------------------------------------------------------- GPU timing
+def time_launches(torch, launch, count: int, warmup: int, stream):
+    """Run `launch(i)` warmup + count times; every timed launch is bracketed by events on
+    `stream`. Returns (total seconds over the timed region, list of per-launch seconds)."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(count)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(count)]
+    for i in range(count):
+        starts[i].record(stream)
+        launch(warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    total = starts[0].elapsed_time(ends[-1]) / 1e3
+    per = [s.elapsed_time(e) / 1e3 for s, e in zip(starts, ends)]
+    return total, per
+
+
+def time_graph(torch, launch, count: int, stream):
+    """Capture `count` launches (launch(i), i = 0..count-1) into one graph on `stream`,
+    replay it once untimed, then time one replay with events. Returns seconds for all
+    `count` launches back to back, with no host in between."""
+    import bandwidth_bound_decode_amd as bbd
+    g = bbd.Graph(stream)
+    with torch.cuda.stream(stream):
+        with g:
+            for i in range(count):
+                launch(i)
+    g.launch(stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    g.launch(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    g.destroy()
+    return start.elapsed_time(end) / 1e3
+
+
+def rotation_arena(torch, w, min_bytes=ROTATION_BYTES):
+    nbytes = w.numel() * w.element_size()
+    copies = max(2, math.ceil(min_bytes / nbytes) + 1)
+    arena = torch.empty((copies,) + tuple(w.shape), dtype=w.dtype, device="cuda")
+    for i in range(copies):
+        arena[i].copy_(w)
+    return arena
+
+
+def bench_gemv(torch, bbd, g, w, x, steps, warmup, segments=(), **plan_opts):
+    """Rotated timing of one GEMV shape (fused when `segments` is given): per-launch event
+    pairs, and the same launches back to back from one graph."""
+    W = w.to("cuda")
+    X = x.to("cuda")
+    arena = rotation_arena(torch, W)
+    plan = bbd.Plan(g.n, g.k, g.m, **plan_opts)
+    ws = plan.alloc_workspace()
+    Y = torch.empty((g.m, g.n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    copies = arena.shape[0]
+    if segments:
+        bounds = [0]
+        for s in segments:
+            bounds.append(bounds[-1] + s)
+        ys = [Y[:, a:b] for a, b in zip(bounds[:-1], bounds[1:])]
+
+        def launch(i, stream=None):
+            wi = arena[i % copies]
+            bbd.fused_run(plan, [(wi[a:b], y) for (a, b), y in
+                                 zip(zip(bounds[:-1], bounds[1:]), ys)], X, ws, stream)
+    else:
+        def launch(i, stream=None):
+            bbd.run(plan, arena[i % copies], X, Y, ws, stream)
+    # per-launch durations: every launch bracketed by its own events (host-paced)
+    _, per = time_launches(torch, launch, steps, warmup, stream)
+    # back to back: the same rotated launches replayed from one graph on a side stream
+    side = torch.cuda.Stream()
+    total = time_graph(torch, lambda i: launch(i, side), steps, side)
+    nb = alg_bytes(g.n, g.k, g.m)
+    res = {"shape": f"{g.n}x{g.k}", "m": g.m, "plan": plan.info, "alg_bytes": nb,
+           "rotation_copies": copies, "us_median": statistics.median(per) * 1e6,
+           "us_p10": pct(per, 0.1) * 1e6, "us_p90": pct(per, 0.9) * 1e6,
+           "us_mean": statistics.fmean(per) * 1e6, "us_per_step_back_to_back": total / steps * 1e6,
+           "TBps_median": nb / statistics.median(per) / 1e12,
+           "TBps_back_to_back": nb * steps / total / 1e12}
+    res["pct_peak_median"] = 100 * res["TBps_median"] * 1e12 / PEAK_HBM
+    del arena
+    return res, total, per, plan
+
+
+def bench_decode_step(torch, bbd, workloads, replays, warmup):
+    from bandwidth_bound_decode_amd.decode_step import Call, Sequence
+    drawn = workloads.draw_decode_step("cuda")
+    calls = [Call(parts, x, [torch.empty((x.shape[0], w.shape[0]), device="cuda")
+                             for w in parts]) for _, parts, x in drawn]
+    seq = Sequence(calls)
+    nb = seq.alg_bytes
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        eager_total, eager_per = time_launches(torch, lambda i: seq.run(stream), replays, warmup,
+                                               stream)
+        seq.capture(stream)
+        graph_total, graph_per = time_launches(torch, lambda i: seq.replay(stream), replays,
+                                               warmup, stream)
+    t_graph = statistics.median(graph_per)
+    t_eager = statistics.median(eager_per)
+    out = {"gemvs": len(calls), "alg_bytes": nb, "weight_bytes": seq.weight_bytes,
+           "replays": replays, "graph_ms_median": t_graph * 1e3,
+           "graph_ms_p10": pct(graph_per, 0.1) * 1e3, "graph_ms_p90": pct(graph_per, 0.9) * 1e3,
+           "graph_TBps": nb / t_graph / 1e12, "graph_mbu": mbu(nb, t_graph, PEAK_HBM),
+           "eager_ms_median": t_eager * 1e3, "eager_mbu": mbu(nb, t_eager, PEAK_HBM),
+           "gate_fraction": 0.80, "meets_gate": mbu(nb, t_graph, PEAK_HBM) >= 0.80}
+    seq.graph.destroy()
+    del seq, calls, drawn
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w, x, runs=3):
+    """The oracle as it stands, on all host threads, over the same full GEMV."""
+    import oracle
+    import numpy as np
+    wb = w.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    xb = x.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    threads = oracle.threads(0)
+    oracle.gemv(wb, xb, nthreads=threads)                 # untimed warm-up
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.gemv(wb, xb, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return t, threads
+
+
+# ---------------------------------------------------------------------------- main
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-replays", type=int, default=20)
+    ap.add_argument("--shape-steps", type=int, default=100)
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-shapes", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this GEMV build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    sys.path.insert(0, HERE)
+    import bandwidth_bound_decode_amd as bbd
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    props = torch.cuda.get_device_properties(0)
+    arch = getattr(props, "gcnArchName", "?")
+    log(f"device: {props.name} {arch} CUs={props.multi_processor_count}")
+
+    # headline: down_proj 4096 x 14336, batch 1
+    cfg = workloads.CONFIGS[1]
+    g = cfg.gemvs[0]
+    (w, x), = workloads.draw_config(cfg)
+    res, total, per, plan = bench_gemv(torch, bbd, g, w, x, args.steps, args.warmup)
+    nb = res["alg_bytes"]
+    value_TBps = nb * args.steps / total / 1e12
+    mean_launch = statistics.fmean(per)
+    achieved_GBps = nb / mean_launch / 1e9
+    log(f"down 4096x14336: {res['us_median']:.2f} us median per launch, "
+        f"{res['TBps_median']:.3f} TB/s; {value_TBps:.3f} TB/s back to back over "
+        f"{args.steps} graph-replayed launches; plan {plan.info}")
+    traffic, traffic_note = counter_traffic(nb)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value_TBps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total / args.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "down_proj GEMV y = W.x, W 4096x14336 bf16 row-major, x bf16, "
+                               "fp32 accumulate and output, batch 1",
+                   "n": g.n, "k": g.k, "m": g.m, "sigma_w": workloads.SIGMA_W,
+                   "sigma_x": workloads.SIGMA_X, "seed": cfg.seed,
+                   "rotation_copies": res["rotation_copies"], "plan": plan.info},
+        "pct_of_peak": round(100 * value_TBps * 1e12 / PEAK_HBM, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved_GBps, 1), "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": round(achieved_GBps * 1e9 / PEAK_HBM, 4),
+                     "traffic": traffic, "traffic_note": traffic_note,
+                     "alg_bytes_per_launch": nb, "launch_us_mean": round(mean_launch * 1e6, 3),
+                     "launch_us_median": round(res["us_median"], 3),
+                     "launch_us_p10": round(res["us_p10"], 3),
+                     "launch_us_p90": round(res["us_p90"], 3)},
+        "device": {"name": props.name, "arch": arch, "cus": props.multi_processor_count,
+                   "peak_hbm_TBps_assumed": PEAK_HBM / 1e12},
+        "h100_context": H100,
+    }
+
+    if not args.skip_cpu:
+        t_cpu, threads = cpu_baseline(w, x)
+        out["cpu_baseline"] = {"value": round(nb / t_cpu / 1e12, 6), "unit": "TB/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": "the full 4096x14336 batch-1 GEMV, fp64 C oracle "
+                                         "(OpenMP over rows), median of 3 runs after 1 warm-up",
+                               "seconds_per_gemv": round(t_cpu, 4),
+                               "host_cpus": len(os.sched_getaffinity(0))}
+        log(f"cpu oracle: {t_cpu * 1e3:.1f} ms per GEMV on {threads} threads")
+
+    if not args.skip_shapes:
+        shapes = []
+        kproj = workloads.CONFIGS[0].gemvs[0]
+        wkp, xkp = workloads.draw_config(workloads.CONFIGS[0])[0]
+        shapes.append(("k_proj", kproj, wkp, xkp, ()))
+        for gg, (ww, xx) in zip(workloads.CONFIGS[2].gemvs, workloads.draw_config(workloads.CONFIGS[2])):
+            shapes.append((gg.name + "_fused", gg, ww, xx, gg.segments))
+        o = workloads.Gemv("o_proj", 4096, 4096)
+        shapes.append(("o_proj", o, *workloads.draw_gemv(o, workloads.generator(7)), ()))
+        lm = workloads.Gemv("lm_head", workloads.VOCAB, workloads.HIDDEN)
+        shapes.append(("lm_head", lm, *workloads.draw_gemv(lm, workloads.generator(8, "cuda"), "cuda"),
+                       ()))
+        for gg, (ww, xx) in zip(workloads.CONFIGS[4].gemvs, workloads.draw_config(workloads.CONFIGS[4])):
+            shapes.append((gg.name, gg, ww, xx, ()))
+        for name, gg, ww, xx, segs in shapes:
+            r, _, _, _ = bench_gemv(torch, bbd, gg, ww, xx, args.shape_steps, 10, segs)
+            r["name"] = name
+            r["plan"] = {k: r["plan"][k] for k in ("splits", "rows_per_wave", "unroll",
+                                                   "grid_x", "grid_y")}
+            for k in list(r):
+                if isinstance(r[k], float):
+                    r[k] = round(r[k], 3)
+            log(f"{name}: {r['us_median']:.2f} us, {r['TBps_median']:.3f} TB/s")
+            out.setdefault("shapes", []).append(r)
+
+    if not args.skip_decode:
+        d = bench_decode_step(torch, bbd, workloads, args.decode_replays, 3)
+        for k in list(d):
+            if isinstance(d[k], float):
+                d[k] = round(d[k], 4)
+        out["decode_step"] = d
+        log(f"decode step: graph {d['graph_ms_median']:.3f} ms (MBU {d['graph_mbu']:.3f}), "
+            f"eager {d['eager_ms_median']:.3f} ms")
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,204 @@
+/*
+ * gemv.h - C ABI of the MI355X (gfx950) decode GEMV library, libbbd_gemv.so.
+ *
+ * The operation is the memory-bound decode GEMV of the decode-GEMV page ("Decode GEMV at
+ * half of HBM bandwidth", inferenceinterviews.com): a row-major [N, K] bf16 weight W times
+ * a bf16 vector x, one fp32-accumulated output per row,
+ *
+ *     Y[m][n] = sum_{k<K} W[n][k] * X[m][k]      for m < M, n < N,
+ *
+ * with M = 1 at decode batch 1 and M <= 16 for the skinny batches of the page's follow-up
+ * on batch 16 ("What interviewers probe next"). bf16 inputs are widened and every
+ * product-sum is accumulated in fp32 (tiled-GEMM page, "What interviewers probe next",
+ * the bf16 question). Y is overwritten, never accumulated into.
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer (W, X, Y, workspace) is a DEVICE pointer on the plan's device.
+ *     Streams are hipStream_t passed as void* (NULL = the legacy default stream, which
+ *     cannot be captured into a graph).
+ *   - Ownership: the caller owns W, X, Y, the workspace and the stream. A plan owns host
+ *     memory only; a segment array is read during the call and not kept. A captured graph
+ *     refers to the caller's buffers, which must outlive it.
+ *   - Errors: every call returns a status; nothing aborts, throws or prints. Arguments are
+ *     validated before any HIP call, so a rejected call enqueues nothing. Launch failures
+ *     come back as GEMV_ERR_DEVICE with the HIP error code in gemv_last_hip_error().
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - gemv_run and gemv_fused_run allocate nothing and never synchronise with the host, so
+ *     they can be captured into a graph. Calls that share a workspace must not overlap.
+ *   - Results are bitwise reproducible for a fixed plan, fixed inputs and a fixed alignment
+ *     class (see gemv_run): split partial sums are combined in a fixed order, never with
+ *     atomics (decode-GEMV page, "What interviewers probe next", the last-bit question).
+ */
+#ifndef BBD_GEMV_H
+#define BBD_GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMV_OK = 0,
+    GEMV_ERR_INVALID_ARG = 1, /* a size, count, leading dimension, option or pointer is bad */
+    GEMV_ERR_MISALIGNED = 2,  /* W/X not 2-byte aligned, or Y/workspace not 4-byte aligned */
+    GEMV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than gemv_workspace_size()   */
+    GEMV_ERR_DEVICE = 4,      /* not a gfx950 device, or a HIP call failed                  */
+    GEMV_ERR_CAPTURE = 5      /* graph capture misuse (legacy stream, not capturing, ...)   */
+} gemv_status;
+
+/* Largest batch a plan accepts (the skinny-batch range of the decode-GEMV page). */
+#define GEMV_MAX_M 16
+/* Largest number of segments gemv_fused_run accepts (QKV uses 3, gate_up 2). */
+#define GEMV_MAX_SEGMENTS 4
+
+typedef struct gemv_plan_s *gemv_plan_t;
+
+/*
+ * Plan overrides; 0 in a field means "choose automatically".
+ *   splits          S, the number of K slices (split-K; decode-GEMV page, "A strong
+ *                   answer", cause 1). 1 <= S <= 64 and every slice must be non-empty.
+ *   rows_per_wave   R, output rows one 64-lane wave reduces together (1, 2 or 4).
+ *   waves_per_block waves in a workgroup (1, 2, 4 or 8).
+ *   unroll          U, independent 16-byte W loads per row each lane issues before using
+ *                   any of them (cause 2 of the same section): 2, 4 or 8.
+ * Not every (M, R, U) combination is compiled; an unsupported one is GEMV_ERR_INVALID_ARG.
+ */
+typedef struct {
+    int splits;
+    int rows_per_wave;
+    int waves_per_block;
+    int unroll;
+} gemv_plan_opts;
+
+/*
+ * The device a plan is sized for. gemv_plan fills it from the runtime; gemv_plan_for takes
+ * it from the caller and makes no HIP call (host-only planning and testing).
+ *   compute_units    CUs the grid is sized to fill (256 on MI355X).
+ *   hbm_bytes_per_s  peak HBM bandwidth (8.0e12 on MI355X).
+ *   latency_s        assumed loaded memory latency for Little's law.
+ */
+typedef struct {
+    int compute_units;
+    double hbm_bytes_per_s;
+    double latency_s;
+} gemv_device_desc;
+
+/* What a plan chose, for tests, tuning and the bench. */
+typedef struct {
+    int splits;             /* S */
+    int rows_per_wave;      /* R */
+    int waves_per_block;
+    int unroll;             /* U */
+    int grid_x;             /* row blocks: ceil(N / (R * waves_per_block)) */
+    int grid_y;             /* = S */
+    int block_threads;      /* 64 * waves_per_block */
+    int64_t slice;          /* K elements per split; a multiple of 8; the last may be short */
+    int depth_bound;        /* h: the most fp32 roundings any product passes through */
+    double bytes_in_flight_per_cu;   /* 16-byte W loads outstanding per CU at full residency */
+    double bytes_in_flight_needed;   /* Little's law per CU: bandwidth * latency / CUs     */
+} gemv_plan_info;
+
+/*
+ * Little's law for memory (decode-GEMV page, "A strong answer"; GPU performance chains
+ * page, "Bytes in flight to reach bandwidth"): the bytes that must be outstanding to sustain
+ * `bytes_per_s` when each request takes `latency_s`. Pure arithmetic.
+ */
+double gemv_bytes_in_flight(double bytes_per_s, double latency_s);
+
+/*
+ * Create a plan for Y[M][N] = X[M][K] . W[N][K]^T on HIP device `device`.
+ * n >= 1, k >= 1, 1 <= m <= GEMV_MAX_M. `opts` may be NULL.
+ * Returns GEMV_ERR_DEVICE if the device is not gfx950 (the only architecture compiled).
+ * On success *out owns a host allocation released by gemv_plan_destroy.
+ */
+gemv_status gemv_plan(gemv_plan_t *out, int64_t n, int64_t k, int m, int device,
+                      const gemv_plan_opts *opts);
+
+/* Same as gemv_plan for an explicit device description; makes no HIP call. */
+gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int m,
+                          const gemv_device_desc *dev, const gemv_plan_opts *opts);
+
+/*
+ * Bytes of workspace gemv_run needs: 0 when S == 1; otherwise a ticket region of
+ * 4 * max(grid_x, 4096) bytes (one 32-bit arrival counter per row block) followed by the
+ * S*M*N fp32 partial sums. 0 for a NULL plan.
+ */
+size_t gemv_workspace_size(gemv_plan_t p);
+
+gemv_status gemv_plan_query(gemv_plan_t p, gemv_plan_info *info);
+
+/* Release a plan (NULL is allowed). Plans are immutable after creation. */
+void gemv_plan_destroy(gemv_plan_t p);
+
+/*
+ * Y[m][n] = sum_k W[n][k] * X[m][k] on `stream`, asynchronously.
+ *   W   bf16 [n][ldw], ldw >= k, 2-byte aligned.
+ *   X   bf16 [m][ldx], ldx >= k, 2-byte aligned (ldx is ignored when m == 1).
+ *   Y   fp32 [m][ldy], ldy >= n, 4-byte aligned; overwritten.
+ *   workspace  device buffer of at least gemv_workspace_size(p) bytes, 4-byte aligned
+ *              (NULL allowed when that size is 0). It holds the split partial sums and
+ *              the tickets that pick, per row block, the workgroup that adds them up.
+ *              It must be zero-filled before its first use; every call that completes
+ *              leaves its tickets at zero again. One workspace can therefore be shared,
+ *              without clearing, by any plans with at most 4096 row blocks (grid_x), in
+ *              any order, as long as their calls do not overlap; every automatically
+ *              chosen split plan on MI355X has fewer than 4096 row blocks.
+ * With S > 1 the S partial sums of each output are added in slice order 0..S-1 by the last
+ * workgroup of its row block to finish, inside the same launch (no second kernel).
+ * When W and X are 16-byte aligned with ldw and ldx multiples of 8 the fast path runs
+ * (one 16-byte load per lane per row step); any other layout runs the unaligned path,
+ * which gives a result within the same tolerance but not bitwise equal to the fast path.
+ */
+gemv_status gemv_run(gemv_plan_t p,
+                     const void *W, int64_t ldw,
+                     const void *X, int64_t ldx,
+                     float *Y, int64_t ldy,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One GEMV over several weight matrices that share X: the fused QKV and gate_up
+ * projections (decode-GEMV page, "A strong answer", cause 3). Segment i holds rows
+ * [sum_{j<i} n_j, sum_{j<=i} n_j) of the plan's N rows:
+ *   W    bf16 [n][ldw], ldw >= k;   Y  fp32 [m][ldy], ldy >= n.
+ * 1 <= nseg <= GEMV_MAX_SEGMENTS and sum n_i == the plan's n. The result is bitwise equal
+ * to gemv_run on the row-concatenation of the segments (same plan, same alignment class).
+ */
+typedef struct {
+    const void *W;
+    int64_t n;
+    int64_t ldw;
+    float *Y;
+    int64_t ldy;
+} gemv_segment;
+
+gemv_status gemv_fused_run(gemv_plan_t p, const gemv_segment *segs, int nseg,
+                           const void *X, int64_t ldx,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Graph capture of a GEMV sequence, so a whole decode step crosses the host-device boundary
+ * once (decode-GEMV page, cause 3; GPU performance chains page, "Launch gaps in a decode
+ * step"). begin starts a thread-local capture on `stream` (not the legacy default stream);
+ * gemv_run / gemv_fused_run calls on that stream are recorded, not executed; end stops the
+ * capture and instantiates an executable graph owned by *out; launch replays it on `stream`.
+ */
+typedef struct gemv_graph_s *gemv_graph_t;
+
+gemv_status gemv_graph_begin(void *stream);
+gemv_status gemv_graph_end(void *stream, gemv_graph_t *out);
+gemv_status gemv_graph_launch(gemv_graph_t g, void *stream);
+void gemv_graph_destroy(gemv_graph_t g);
+
+/* A static description of a status code ("unknown status" for anything else). */
+const char *gemv_status_string(gemv_status s);
+
+/* The hipError_t behind this thread's last GEMV_ERR_DEVICE / GEMV_ERR_CAPTURE (0 if none). */
+int gemv_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BBD_GEMV_H */

@@ -1,0 +1,177 @@
+"""CPU tests of the C ABI: every declared symbol is exported, and invalid arguments come back
+as the documented status before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import bandwidth_bound_decode_amd as bbd
+from bandwidth_bound_decode_amd._binding import DeviceDesc, PlanOpts, Segment, Status
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemv.h")
+MI355X = (256, 8.0e12, 1.0e-6)
+FAKE = 0x7F0000000000          # 16-byte aligned stand-in for a device address (never touched)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("gemv_plan", "gemv_run", "gemv_fused_run", "gemv_graph_begin",
+                     "gemv_graph_end", "gemv_graph_launch", "gemv_graph_destroy",
+                     "gemv_workspace_size", "gemv_plan_query", "gemv_plan_destroy",
+                     "gemv_status_string", "gemv_last_hip_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", bbd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b[TW]\s+(\S+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(bbd.SIGNATURES) == names, "binding signatures out of sync with the header"
+    for n in names:
+        assert hasattr(bbd.lib(), n)
+
+
+def test_library_targets_gfx950_only(tmp_path):
+    """The device code object bundled in the library is for gfx950 and nothing else."""
+    fatbin = tmp_path / "fatbin"
+    # explicit output file: objcopy without one rewrites its input in place
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", bbd.LIB_PATH,
+                    str(fatbin)], check=True, capture_output=True)
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o",
+                          f"--input={fatbin}"], capture_output=True, text=True, check=True)
+    targets = [t for t in out.stdout.split() if "amdgcn" in t]
+    assert targets == ["hipv4-amdgcn-amd-amdhsa--gfx950"], targets
+
+
+def test_status_strings():
+    lib = bbd.lib()
+    seen = set()
+    for s in Status:
+        text = lib.gemv_status_string(int(s)).decode()
+        assert text and text != "unknown status"
+        seen.add(text)
+    assert len(seen) == len(Status)
+    assert lib.gemv_status_string(99).decode() == "unknown status"
+
+
+def host_plan(n, k, m=1, **opts):
+    h = ctypes.c_void_p()
+    o = PlanOpts(opts.get("splits", 0), opts.get("rows_per_wave", 0),
+                 opts.get("waves_per_block", 0), opts.get("unroll", 0))
+    d = DeviceDesc(*MI355X)
+    st = bbd.lib().gemv_plan_for(ctypes.byref(h), n, k, m, ctypes.byref(d), ctypes.byref(o))
+    return st, h
+
+
+@pytest.fixture
+def plan_split():
+    st, h = host_plan(1024, 4096, 1)      # k_proj: the plan splits K
+    assert st == Status.OK
+    yield h
+    bbd.lib().gemv_plan_destroy(h)
+
+
+@pytest.fixture
+def plan_m3():
+    st, h = host_plan(64, 1000, 3, splits=1)
+    assert st == Status.OK
+    yield h
+    bbd.lib().gemv_plan_destroy(h)
+
+
+def run(h, W=FAKE, ldw=4096, X=FAKE, ldx=4096, Y=FAKE, ldy=1024, ws=FAKE, ws_bytes=1 << 20):
+    return bbd.lib().gemv_run(h, W, ldw, X, ldx, Y, ldy, ws, ws_bytes, None)
+
+
+def test_plan_arguments():
+    for n, k, m in ((0, 8, 1), (8, 0, 1), (8, 8, 0), (8, 8, 17), (-1, 8, 1)):
+        assert host_plan(n, k, m)[0] == Status.INVALID_ARG
+    assert host_plan(8, 8, 1, splits=-1)[0] == Status.INVALID_ARG
+    assert host_plan(8, 8, 1, rows_per_wave=3)[0] == Status.INVALID_ARG     # not compiled
+    assert host_plan(8, 8, 16, unroll=8)[0] == Status.INVALID_ARG
+    assert host_plan(8, 8, 1, waves_per_block=3)[0] == Status.INVALID_ARG
+    assert host_plan(8, 8, 1, splits=65)[0] == Status.INVALID_ARG
+    assert host_plan(8, 129, 1, splits=7)[0] == Status.INVALID_ARG         # empty slice
+    lib = bbd.lib()
+    d = DeviceDesc(0, 8e12, 1e-6)
+    h = ctypes.c_void_p()
+    assert lib.gemv_plan_for(ctypes.byref(h), 8, 8, 1, ctypes.byref(d), None) == Status.INVALID_ARG
+    assert lib.gemv_plan_for(None, 8, 8, 1, ctypes.byref(DeviceDesc(*MI355X)), None) \
+        == Status.INVALID_ARG
+    # gemv_plan rejects bad sizes before asking the runtime about the device
+    assert lib.gemv_plan(ctypes.byref(h), 0, 8, 1, 0, None) == Status.INVALID_ARG
+    assert lib.gemv_plan(ctypes.byref(h), 8, 8, 17, 0, None) == Status.INVALID_ARG
+    assert lib.gemv_plan_query(None, None) == Status.INVALID_ARG
+    assert lib.gemv_workspace_size(None) == 0
+    lib.gemv_plan_destroy(None)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
+def test_plan_without_device_is_a_device_error():
+    h = ctypes.c_void_p()
+    assert bbd.lib().gemv_plan(ctypes.byref(h), 8, 8, 1, 0, None) == Status.DEVICE
+    assert not h
+
+
+def test_run_validation(plan_split, plan_m3):
+    h = plan_split
+    # a 4096-slot ticket region, then S=4 x M=1 x N=1024 fp32 partials
+    assert bbd.lib().gemv_workspace_size(h) == 4096 * 4 + 4 * 1024 * 4
+    assert run(None) == Status.INVALID_ARG
+    assert run(h, W=None) == Status.INVALID_ARG
+    assert run(h, X=None) == Status.INVALID_ARG
+    assert run(h, Y=None) == Status.INVALID_ARG
+    assert run(h, ldw=4095) == Status.INVALID_ARG
+    assert run(h, ldy=1023) == Status.INVALID_ARG
+    assert run(h, W=FAKE + 1) == Status.MISALIGNED
+    assert run(h, X=FAKE + 3) == Status.MISALIGNED
+    assert run(h, Y=FAKE + 2) == Status.MISALIGNED
+    assert run(h, ws=None) == Status.WORKSPACE
+    assert run(h, ws_bytes=4096 * 4 + 4 * 1024 * 4 - 1) == Status.WORKSPACE
+    assert run(h, ws=FAKE + 2) == Status.MISALIGNED
+    # batched plan: X rows need ldx >= k; ldx is not checked for a single vector
+    assert run(plan_m3, ldw=1000, ldx=999, ldy=64, ws=None, ws_bytes=0) == Status.INVALID_ARG
+
+
+def test_fused_validation(plan_split):
+    lib = bbd.lib()
+    h = plan_split
+
+    def fused(segs, X=FAKE, ws=FAKE, ws_bytes=1 << 20, nseg=None):
+        arr = (Segment * max(len(segs), 1))(*segs)
+        return lib.gemv_fused_run(h, arr, len(segs) if nseg is None else nseg, X, 4096, ws,
+                                  ws_bytes, None)
+
+    good = [Segment(FAKE, 512, 4096, FAKE, 512), Segment(FAKE, 512, 4096, FAKE, 512)]
+    assert fused(good, nseg=0) == Status.INVALID_ARG
+    assert fused(good * 3, nseg=5) == Status.INVALID_ARG
+    assert fused(good[:1]) == Status.INVALID_ARG                 # 512 rows != plan's 1024
+    assert fused([Segment(FAKE, 1024, 4096, FAKE, 1024), Segment(FAKE, 0, 4096, FAKE, 1)]) \
+        == Status.INVALID_ARG
+    assert fused([good[0], Segment(FAKE, 512, 4000, FAKE, 512)]) == Status.INVALID_ARG
+    assert fused([good[0], Segment(FAKE + 1, 512, 4096, FAKE, 512)]) == Status.MISALIGNED
+    assert fused(good, ws=None) == Status.WORKSPACE
+    assert lib.gemv_fused_run(h, None, 2, FAKE, 4096, FAKE, 1 << 20, None) == Status.INVALID_ARG
+
+
+def test_graph_argument_errors():
+    lib = bbd.lib()
+    assert lib.gemv_graph_begin(None) == Status.CAPTURE          # legacy default stream
+    assert lib.gemv_graph_end(None, None) == Status.INVALID_ARG
+    out = ctypes.c_void_p()
+    assert lib.gemv_graph_end(None, ctypes.byref(out)) == Status.CAPTURE
+    assert lib.gemv_graph_launch(None, None) == Status.INVALID_ARG
+    lib.gemv_graph_destroy(None)

@@ -1,0 +1,48 @@
+"""GPU parity of skinny batches (M = 1..16): within tolerance of the oracle, and every row of
+Y bitwise equal to the batch-1 run on that row of X (the split count and the per-row
+summation order do not depend on M)."""
+import pytest
+import torch
+
+import bandwidth_bound_decode_amd as bbd
+import workloads
+from gpu_helpers import bits_equal, device_matrix, draw, gemv, oracle_check
+
+pytestmark = pytest.mark.gpu
+
+
+def rows_match_batch_one(W, X, Y):
+    for i in range(X.shape[0]):
+        y1, _ = gemv(W, X[i:i + 1])
+        assert bits_equal(Y[i:i + 1], y1), f"batch row {i} differs from its batch-1 run"
+
+
+def test_skinny_config():
+    cfg = workloads.CONFIGS[4]
+    for g, (w, x) in zip(cfg.gemvs, workloads.draw_config(cfg)):
+        W, X = device_matrix(w), device_matrix(x)
+        Y, p = gemv(W, X)
+        print(g.name, p.info, flush=True)
+        oracle_check(W, X, Y, g.name)
+        rows_match_batch_one(W, X, Y)
+
+
+@pytest.mark.parametrize("m", range(1, 17))
+def test_every_batch_size(m):
+    n, k = 300, 5000
+    w, x = draw(n, k, m, seed=100 + m)
+    W, X = device_matrix(w), device_matrix(x)
+    Y, _ = gemv(W, X)
+    oracle_check(W, X, Y, f"m={m}")
+    rows_match_batch_one(W, X, Y)
+
+
+@pytest.mark.parametrize("m", [2, 3, 7, 16])
+def test_batch_unaligned(m):
+    n, k = 45, 3001
+    w, x = draw(n, k, m, seed=200 + m)
+    W = device_matrix(w, ld=3003, offset=1)
+    X = device_matrix(x, ld=3005, offset=3)
+    Y, _ = gemv(W, X)
+    oracle_check(W, X, Y, f"unaligned m={m}")
+    rows_match_batch_one(W, X, Y)

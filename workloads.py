@@ -114,3 +114,24 @@ def bf16_bits(t: torch.Tensor):
     """The raw bf16 bit patterns of a tensor as a contiguous host uint16 numpy array."""
     assert t.dtype == torch.bfloat16
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view("uint16")
+
+
+def draw_decode_step(device: str | torch.device = "cuda", layers: int = LAYERS,
+                     seed: int | None = None):
+    """Draw the decode-step sequence: for each GEMV in stream order, its weight (as separate
+    contiguous tensors, one per segment of a fused projection) and its input vector.
+
+    Returns a list of (Gemv, [W parts], X). About 15 GB of weights at 32 layers, so draw on
+    the GPU.
+    """
+    gen = generator(CONFIGS[3].seed if seed is None else seed, device)
+    out = []
+    for g in decode_step_gemvs(layers):
+        w, x = draw_gemv(g, gen, device)
+        if g.segments:
+            parts = [t.clone() for t in torch.split(w, list(g.segments), 0)]
+            del w
+        else:
+            parts = [w]
+        out.append((g, parts, x))
+    return out
