@@ -168,7 +168,10 @@ __device__ __forceinline__ void finish(const Problem &p, float (&acc)[R][M], int
         int row = row_first + r;
         if (row < p.n) {
             if (p.partial) {
-                p.partial[((int64_t)split * M + m) * p.n + row] = out;
+                // Agent-scope store: coherent across the XCDs' separate L2 caches, so the
+                // workgroup that adds the partials up can read it from any XCD.
+                __hip_atomic_store(p.partial + ((int64_t)split * M + m) * p.n + row, out,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             } else {
                 RowRef ref = locate(p, row);
                 ref.y[(int64_t)m * ref.ldy] = out;
@@ -180,21 +183,27 @@ __device__ __forceinline__ void finish(const Problem &p, float (&acc)[R][M], int
 // Pass 2 of split-K, run by the whole workgroup after its waves stored their partials.
 // The last of the S workgroups of row block blockIdx.x to arrive sums the partials of the
 // block's rows in slice order and leaves the ticket at zero for the next call.
+//
+// Ordering without cache maintenance: partials are written and read with agent-scope
+// (device-coherent) stores and loads, every wave waits until its stores have completed
+// before the workgroup barrier, and only then does one lane take the ticket. A workgroup
+// that draws the last ticket therefore finds every other slice's partials in coherent
+// memory. L2 write-back / invalidate fences are avoided on purpose: issued per workgroup
+// they cost more than the whole GEMV.
 __device__ __forceinline__ void combine_if_last(const Problem &p, int m_count,
                                                 int rows_per_block)
 {
     __shared__ unsigned s_last;
-    __threadfence();        // this wave's partial stores are complete and visible device-wide
+    __builtin_amdgcn_s_waitcnt(0);      // this wave's partial stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned ticket = __hip_atomic_fetch_add(p.tickets + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
+        unsigned ticket = __hip_atomic_fetch_add(p.tickets + blockIdx.x, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
         s_last = ticket == gridDim.y - 1;
     }
     __syncthreads();
     if (!s_last)
         return;
-    __threadfence();        // acquire: the other slices' partials are visible to this CU
     const int row0 = blockIdx.x * rows_per_block;
     const int rows = min(rows_per_block, p.n - row0);
     const int64_t plane = (int64_t)m_count * p.n;   // one slice's partials
@@ -202,9 +211,9 @@ __device__ __forceinline__ void combine_if_last(const Problem &p, int m_count,
         const int m = t / rows;
         const int row = row0 + (t - m * rows);
         const float *src = p.partial + (int64_t)m * p.n + row;
-        float v = src[0];
+        float v = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (unsigned sl = 1; sl < gridDim.y; ++sl)
-            v += src[sl * plane];
+            v += __hip_atomic_load(src + sl * plane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         RowRef ref = locate(p, row);
         ref.y[(int64_t)m * ref.ldy] = v;
     }
@@ -280,18 +289,33 @@ __device__ __forceinline__ void fast_rows(const Problem &p, int row_first, int l
                 for (int m = 0; m < M; ++m)
                     acc[r][m] = dot8(wv[u][r], xv[u][m], acc[r][m]);
     }
-    for (; step < full; ++step) {
-        u32x4 wv[R];
+    if (step < full) {
+        // Fewer than U full steps left: issue them as one burst too (wave-uniform
+        // predicates), so the remainder costs one memory latency, not one per step.
+        const int rest = full - step;
+        u32x4 wv[U][R];
+        u32x4 xv[U][M];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            wv[r] = load_stream(wrow[r] + 8 * (lane + 64 * step));
+        for (int u = 0; u < U; ++u)
+            if (u < rest)
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            u32x4 xv = load_cached(xk + m * p.ldx + 8 * (lane + 64 * step));
+                for (int r = 0; r < R; ++r)
+                    wv[u][r] = load_stream(wrow[r] + 8 * (lane + 64 * (step + u)));
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-                acc[r][m] = dot8(wv[r], xv, acc[r][m]);
-        }
+        for (int u = 0; u < U; ++u)
+            if (u < rest)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    xv[u][m] = load_cached(xk + m * p.ldx + 8 * (lane + 64 * (step + u)));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u < rest)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        acc[r][m] = dot8(wv[u][r], xv[u][m], acc[r][m]);
     }
     // Last, partial wave step: only lanes whose vector lies inside the slice.
     const int v_last = lane + 64 * full;

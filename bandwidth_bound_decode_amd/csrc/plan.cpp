@@ -40,23 +40,35 @@ namespace {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// Defaults per batch size: (rows per wave, unroll). Larger M spends VGPRs on X vectors
-// and accumulators, so the W unroll shrinks.
-void default_tile(int m, int *r, int *u)
+// Default tile per batch size and shape: (rows per wave R, unroll U, waves per workgroup).
+// At M = 1 every wave keeps R x U = 8 loads (8 KiB) in flight. A row of up to 8 wave steps
+// (K <= 4096) is fetched by one single-row wave in one burst; longer rows go two per wave in
+// bursts of 4 when N leaves at least 8 such waves per CU (fewer, fuller waves and half the x
+// traffic), else one per wave in bursts of 8. Larger M spends VGPRs on X vectors and
+// accumulators, so the W unroll shrinks. Chosen from measured sweeps on MI355X; every choice
+// gives bitwise the same result.
+void default_tile(int m, int64_t n, int64_t k, int cus, int *r, int *u, int *waves)
 {
+    int64_t steps = (k + kWaveStep - 1) / kWaveStep;
     if (m == 1) {
-        *r = 2;
-        *u = 4;
+        if (steps > 8 && n >= (int64_t)8 * 2 * cus) {
+            *r = 2;
+            *u = 4;
+        } else {
+            *r = 1;
+            *u = 8;
+        }
+        *waves = 1;
     } else if (m <= 4) {
         *r = 2;
         *u = 4;
+        *waves = 4;
     } else {
         *r = 2;
         *u = 2;
+        *waves = 4;
     }
 }
-
-constexpr int kDefaultWaves = 4;
 
 // K elements per split for S splits: wave-step aligned when a slice spans more than one
 // wave-wide step, so every lane of every slice but the last walks the same vectors.
@@ -104,48 +116,57 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     if (o.splits < 0 || o.rows_per_wave < 0 || o.waves_per_block < 0 || o.unroll < 0)
         return GEMV_ERR_INVALID_ARG;
 
-    int r, u;
-    default_tile(m, &r, &u);
+    int r, u, waves;
+    default_tile(m, n, k, dev->compute_units, &r, &u, &waves);
     if (o.rows_per_wave)
         r = o.rows_per_wave;
     if (o.unroll)
         u = o.unroll;
-    int waves = o.waves_per_block ? o.waves_per_block : kDefaultWaves;
+    if (o.waves_per_block)
+        waves = o.waves_per_block;
     if (!valid_waves(waves) || !variant_supported(m, r, u))
         return GEMV_ERR_INVALID_ARG;
 
     // The split count depends on N, K and the machine only - not on M - so that every
-    // row of a batched result is summed in the same order as the batch-1 result.
-    int r1, u1;
-    default_tile(1, &r1, &u1);
-    int64_t rows_per_block_s = (int64_t)(o.rows_per_wave ? r : r1) * waves;
-    int64_t row_blocks_s = ceil_div(n, rows_per_block_s);
+    // row of a batched result is summed in the same order as the batch-1 result. It is
+    // decided on the batch-1 tile's wave count: one wave per R rows.
+    int r1, u1, w1;
+    default_tile(1, n, k, dev->compute_units, &r1, &u1, &w1);
+    int64_t waves_s1 = ceil_div(n, o.rows_per_wave ? r : r1);
 
     int s;
     int64_t slice;
     if (o.splits) {
+        // A forced split count gets slices aligned to 8 elements only, so that any count
+        // that leaves no slice empty is accepted.
         s = o.splits;
         if (s > kMaxSplits)
             return GEMV_ERR_INVALID_ARG;
-        slice = slice_for(k, s);
+        slice = round_up(ceil_div(k, s), kVecElems);
         if (ceil_div(k, slice) != s)   // some slice would be empty
             return GEMV_ERR_INVALID_ARG;
     } else {
-        int64_t target = (int64_t)kTargetBlocksPerCU * dev->compute_units;
-        int64_t want = row_blocks_s >= target ? 1 : ceil_div(target, row_blocks_s);
+        // No split while the rows alone give every CU a few waves: a split adds a dependent
+        // chain of memory round trips (partial store, ticket, partial loads) to the tail.
+        // Below that, split until every CU has kTargetWavesPerCU waves.
+        int64_t floor_waves = (int64_t)kMinWavesPerCU * dev->compute_units;
+        int64_t target = (int64_t)kTargetWavesPerCU * dev->compute_units;
+        int64_t want = waves_s1 >= floor_waves ? 1 : ceil_div(target, waves_s1);
         int64_t cap = k / kMinSlice > 1 ? k / kMinSlice : 1;
         if (want > cap)
             want = cap;
         if (want > kMaxSplits)
             want = kMaxSplits;
-        s = (int)want;
-        slice = slice_for(k, s);
-        s = (int)ceil_div(k, slice);
-        // Split further if one slice would exceed the summation-depth bound.
-        while (depth_for(slice, s) > kMaxDepth && s < kMaxSplits) {
-            ++s;
-            slice = slice_for(k, s);
+        // Take the first candidate count, from `want` up, whose slices meet the
+        // summation-depth bound (the realised count can be lower than the candidate when
+        // slices round up to whole wave steps).
+        s = 0;
+        slice = 0;
+        for (int cand = (int)want; cand <= kMaxSplits; ++cand) {
+            slice = slice_for(k, cand);
             s = (int)ceil_div(k, slice);
+            if (depth_for(slice, s) <= kMaxDepth)
+                break;
         }
         // K beyond ~720k elements cannot meet the bound with 64 slices: refuse rather than
         // return a plan whose result may miss the tolerance.

@@ -18,7 +18,8 @@ constexpr int kMaxWavesPerCU = 32;      // 4 SIMDs x 8 waves
 constexpr int kMaxSplits = 64;
 
 // Planning constants (tunable, see the plan rule in plan.cpp).
-constexpr int kTargetBlocksPerCU = 4;   // "several waves" of workgroups on every CU
+constexpr int kMinWavesPerCU = 1;       // no split while N / R gives this many waves per CU
+constexpr int kTargetWavesPerCU = 4;    // a split aims for this many waves per CU
 constexpr int64_t kMinSlice = 1024;     // never split K finer than this many elements
 constexpr int kMaxDepth = 160;          // gamma_160 (u = 2^-24) = 9.54e-6 < 1e-5
 constexpr double kDefaultLatency = 1.0e-6;   // assumed loaded HBM latency on MI355X

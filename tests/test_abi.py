@@ -78,7 +78,7 @@ def host_plan(n, k, m=1, **opts):
 
 @pytest.fixture
 def plan_split():
-    st, h = host_plan(1024, 4096, 1)      # k_proj: the plan splits K
+    st, h = host_plan(1024, 4096, 1, splits=4)      # k_proj shape, K split in 4
     assert st == Status.OK
     yield h
     bbd.lib().gemv_plan_destroy(h)

@@ -199,7 +199,7 @@ def test_misaligned_pointers_rejected():
 def test_workspace_checks_on_device():
     w, x = draw(1024, 4096, 1, seed=2)
     W, X = device_matrix(w), device_matrix(x)
-    p = bbd.Plan(1024, 4096, 1)
+    p = bbd.Plan(1024, 4096, 1, splits=4)
     assert p.workspace_size > 0
     Y = output(1, 1024)
     with pytest.raises(bbd.GemvError) as e:
@@ -214,7 +214,7 @@ def test_workspace_checks_on_device():
 def test_one_workspace_shared_by_two_plans():
     a = draw(1024, 4096, 1, seed=3)
     b = draw(4096, 14336, 1, seed=4)
-    pa, pb = bbd.Plan(1024, 4096, 1), bbd.Plan(4096, 14336, 1, splits=4)
+    pa, pb = bbd.Plan(1024, 4096, 1, splits=2), bbd.Plan(4096, 14336, 1, splits=4)
     ws = torch.zeros(max(pa.workspace_size, pb.workspace_size), dtype=torch.uint8, device="cuda")
     Wa, Xa, Wb, Xb = (device_matrix(t) for t in (*a, *b))
     Ya, Yb = output(1, 1024), output(1, 4096)

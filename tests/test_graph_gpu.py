@@ -48,11 +48,13 @@ def test_small_graph():
     """A short mixed sequence: split and unsplit plans, a fused call, a batch of 3."""
     drawn = []
     for i, (n, k, m, segs) in enumerate([(1024, 4096, 1, ()), (600, 4096, 1, (100, 500)),
-                                         (4096, 14336, 1, ()), (77, 1000, 3, ())]):
+                                         (256, 14336, 1, ()), (4096, 14336, 1, ()),
+                                         (77, 1000, 3, ())]):
         w, x = draw(n, k, m, seed=50 + i)
         parts = [device_matrix(p) for p in (torch.split(w, list(segs)) if segs else [w])]
         drawn.append((None, parts, device_matrix(x)))
     seq = make_sequence(drawn)
+    assert any(c.plan.info["splits"] > 1 for c in seq.calls), "want a split-K call in the graph"
     eager = replay_matches_eager(seq)
     for (_, parts, x), y in zip(drawn, eager):
         oracle_check(torch.cat(parts, 0), x, y, "small graph")

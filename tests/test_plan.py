@@ -79,12 +79,15 @@ def test_mi355x_plans(n, k, m):
     assert info["depth_bound"] <= 160
     h = info["depth_bound"]
     assert h * 2.0 ** -24 / (1 - h * 2.0 ** -24) < 1e-5
-    # "several waves" of workgroups on every CU, or no split because rows alone cover it
-    blocks = info["grid_x"] * info["grid_y"]
+    # "several waves" of workgroups on every CU, or no split because rows alone cover it.
+    # The split count is decided on the batch-1 tile (so it does not depend on M).
+    b1 = plan(n, k, 1).info
+    blocks1 = b1["grid_x"] * b1["grid_y"]
+    assert b1["splits"] == s
     if s == 1:
-        assert info["grid_x"] >= 4 * 256 or k < 2 * 1024
+        assert b1["grid_x"] >= 4 * 256 or k < 2 * 1024
     else:
-        assert blocks >= 4 * 256 or s == k // 1024
+        assert blocks1 >= 4 * 256 or s == k // 1024
 
 
 def test_split_count_does_not_depend_on_batch():
@@ -97,7 +100,10 @@ def test_split_count_does_not_depend_on_batch():
 def test_split_rule_examples():
     assert plan(128256, 4096).info["splits"] == 1          # LM head: no split
     assert plan(28672, 4096).info["splits"] == 1           # gate_up: no split
-    assert plan(1024, 4096).info["splits"] > 1             # k_proj: too few rows
+    assert plan(1024, 4096).info["splits"] == 1            # k_proj: 4 waves per CU already
+    assert plan(4096, 14336).info["splits"] == 1           # down_proj: 8 waves per CU
+    assert plan(256, 14336).info["splits"] == 1            # one wave per CU: still no split
+    assert plan(64, 14336).info["splits"] > 1              # too few rows: split K
     assert plan(7, 129).info["splits"] == 1                # too short to split
     long_k = plan(64, 1 << 19).info
     assert long_k["splits"] >= 2 and long_k["depth_bound"] <= 160   # accuracy forces a split
@@ -122,3 +128,22 @@ def test_bytes_in_flight_report():
     per_cu = min(math.ceil(waves / 256), 32)
     assert i["bytes_in_flight_per_cu"] == per_cu * i["unroll"] * i["rows_per_wave"] * 1024
     assert i["bytes_in_flight_per_cu"] >= i["bytes_in_flight_needed"]
+
+
+@pytest.mark.timeout(120)
+def test_plan_search_terminates_for_any_shape():
+    """Planning is a bounded search: every (N, K) either yields a plan that meets the depth
+    bound or is refused, quickly (a cycling split search once hung here)."""
+    import random
+    rng = random.Random(0)
+    ks = sorted({1, 7, 8, 9, 511, 512, 513, 4095, 4096, 4097, 14336, 14337, 18944, 18945,
+                 65536, 262144, 524288, 720896, 720897, 1 << 20} |
+                {rng.randrange(1, 1 << 21) for _ in range(300)})
+    for k in ks:
+        for n in (1, 7, 64, 255, 256, 511, 1024, 4096, 128256):
+            try:
+                info = plan(n, k).info
+            except bbd.GemvError:
+                assert k > 700000, (n, k)
+                continue
+            assert info["depth_bound"] <= 160 and info["splits"] >= 1, (n, k)
