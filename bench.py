@@ -31,8 +31,7 @@ PEAK_HBM = 8.0e12                 # MI355X HBM3E, published peak, B/s
 METRIC = "achieved HBM TB/s and % of peak, bf16 GEMV batch 1 at Llama-8B shapes"
 ROTATION_BYTES = 1.0e9            # >= 1 GB of distinct weights per rotation arena
 COUNTERS_FILE = os.path.join(HERE, "profiles", "counters_down_4096x14336.json")
-KERNEL_SOURCES = [os.path.join(HERE, "bandwidth_bound_decode_amd", "csrc", f)
-                  for f in ("gemv.hip", "plan.cpp", "plan.h")]
+KERNEL_SOURCE = os.path.join(HERE, "bandwidth_bound_decode_amd", "csrc", "gemv.hip")
 
 # The pages' H100 SXM context (decode-GEMV page and GPU performance chains page).
 H100 = {"hbm_TBps": 3.35, "sms": 132, "k_proj_transfer_us_at_peak": 2.5,
@@ -67,26 +66,26 @@ def ridge(flops_per_s: float, bytes_per_s: float) -> float:
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
-def counter_traffic(launch_bytes_expected: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if there is
-    none or the kernels changed since it was taken."""
+def counter_traffic(plan_info: dict):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when there
+    is none, or the kernel source or the launch configuration changed since it was taken."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None, "no counter summary"
     if c.get("kernel_source_sha256") != kernel_source_hash():
-        return None, "kernel sources changed since the counters were taken"
+        return None, "kernel source changed since the counters were taken"
+    if any(plan_info.get(k) != v for k, v in c.get("plan", {}).items()):
+        return None, "launch configuration changed since the counters were taken"
     fetch = c["fetch_kib_per_launch"] * 1024 * c["fetch_scale"]
     write = c["write_kib_per_launch"] * 1024 * c["write_scale"]
-    return fetch + write, f"rocprofv3 FETCH_SIZE+WRITE_SIZE scaled by copy calibration"
+    return round(fetch + write), ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, scaled by a "
+                                  "plain copy of known size (profiles/counters_down_4096x14336.json)")
 
 
 def log(msg: str):
@@ -278,7 +277,7 @@ def main(argv=None):
     log(f"down 4096x14336: {res['us_median']:.2f} us median per launch, "
         f"{res['TBps_median']:.3f} TB/s; {value_TBps:.3f} TB/s back to back over "
         f"{args.steps} graph-replayed launches; plan {plan.info}")
-    traffic, traffic_note = counter_traffic(nb)
+    traffic, traffic_note = counter_traffic(plan.info)
 
     out = {
         "metric": METRIC,
