@@ -7,6 +7,7 @@ from forming them out of scalar float code.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 import tempfile
@@ -27,14 +28,48 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror",
              f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+RESOURCE_REPORT = os.path.join(LIB_DIR, "kernel_resources.json")
+REMARK = "[-Rpass-analysis=kernel-resource-usage]"
+
+
 def _run(cmd):
     proc = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l)
+    lines = [l for l in proc.stderr.splitlines() if noise not in l]
+    remarks = [l for l in lines if REMARK in l]
+    # drop the remarks and the source excerpts the compiler prints under each of them
+    err = "\n".join(l for l in lines if REMARK not in l and "remark:" not in l
+                    and not re.match(r"^\s*(\d+\s*)?[|^]", l))
     if proc.returncode != 0:
         raise RuntimeError(f"build failed: {' '.join(cmd)}\n{err}")
     if err.strip():
         sys.stderr.write(err + "\n")
+    return remarks
+
+
+def _resources(remarks):
+    """Per-kernel resource usage from the compiler's kernel-resource-usage remarks."""
+    kernels, cur = {}, None
+    for line in remarks:
+        body = line.split("remark:", 1)[1].replace(REMARK, "").strip()
+        key, _, val = body.partition(":")
+        key, val = key.strip(), val.strip()
+        if key == "Function Name":
+            cur = kernels.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = val
+    return kernels
+
+
+def _check_resources(kernels):
+    """Refuse a library in which any kernel uses scratch memory or spills VGPRs. (SGPR spills
+    land in VGPR lanes, not memory; they are recorded in the report but allowed.)"""
+    if not kernels:
+        raise RuntimeError("the compiler reported no kernel resource usage")
+    bad = [name for name, r in kernels.items()
+           if r.get("ScratchSize [bytes/lane]", "0") != "0" or r.get("VGPRs Spill", "0") != "0"]
+    if bad:
+        raise RuntimeError(f"kernels using scratch memory or spilling VGPRs: {bad[:5]}")
 
 
 def build(out: str = LIB_PATH, save_temps: str | None = None) -> str:
@@ -44,19 +79,23 @@ def build(out: str = LIB_PATH, save_temps: str | None = None) -> str:
         plan_o = os.path.join(tmp, "plan.o")
         gemv_o = os.path.join(tmp, "gemv.o")
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
-        extra = [f"-save-temps={save_temps}"] if save_temps else []
-        cwd = os.getcwd()
-        try:
-            if save_temps:
-                os.makedirs(save_temps, exist_ok=True)
-                os.chdir(save_temps)
-            _run([HIPCC, *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, "gemv.hip"), "-o", gemv_o])
-        finally:
-            os.chdir(cwd)
+        remarks = _run([HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage",
+                        "-c", os.path.join(CSRC, "gemv.hip"), "-o", gemv_o])
+        if save_temps:
+            # the device assembly, for reading the generated code
+            os.makedirs(save_temps, exist_ok=True)
+            _run([HIPCC, *HIP_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, "gemv.hip"),
+                  "-o", os.path.join(save_temps, "gemv-hip-amdgcn-amd-amdhsa-gfx950.s")])
         tmp_out = out + ".tmp"
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", plan_o, gemv_o,
               "-o", tmp_out])
+        kernels = _resources(remarks)
+        _check_resources(kernels)
         os.replace(tmp_out, out)
+    if out == LIB_PATH:
+        import json
+        with open(RESOURCE_REPORT, "w") as f:
+            json.dump(kernels, f, indent=1, sort_keys=True)
     return out
 
 

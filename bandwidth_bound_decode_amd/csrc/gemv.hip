@@ -27,6 +27,7 @@
 // There is no LDS staging of W: a GEMV has no reuse of W (the page's common mistakes).
 #include <hip/hip_runtime.h>
 
+#include <limits.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -45,20 +46,27 @@ struct Seg {
     int64_t ldw;
     float *y;           // row 0 of the segment's output
     int64_t ldy;
-    int32_t row0;       // first global row of the segment
+    int32_t row0;       // first global row of the segment (INT32_MAX when unused)
     int32_t pad;
 };
 
+// Kernel arguments. The first 64 bytes hold everything a single-segment launch needs, so
+// its prologue is one batch of scalar loads; the other segments are read only by fused
+// launches (nseg > 1).
 struct Problem {
-    Seg seg[GEMV_MAX_SEGMENTS];
+    const uint16_t *w0;     // segment 0
+    int64_t ldw0;
+    float *y0;
+    int64_t ldy0;
     const uint16_t *x;
     int64_t ldx;
-    float *partial;     // [S][M][N] when the plan splits K, else null
-    unsigned *tickets;  // [grid_x] arrival counters, zero between calls (split plans only)
-    int32_t nseg;
     int32_t n;
     int32_t k;
     int32_t slice;
+    int32_t nseg;
+    Seg seg[GEMV_MAX_SEGMENTS];       // all segments, segment 0 repeated (fused launches only)
+    float *partial;     // [S][M][N] when the plan splits K, else null
+    unsigned *tickets;  // [grid_x] arrival counters, zero between calls (split plans only)
 };
 
 // ---------------------------------------------------------------------------- helpers
@@ -122,33 +130,58 @@ __device__ __forceinline__ float lane63(float v)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Segment holding global row `row` (segments are in row order). Select chain, no
-// dynamic indexing, so it works for uniform and per-lane rows alike.
+// Segment holding global row `row`. The single-segment instances (MULTI = false, every
+// gemv_run) read only the argument header, so their prologue is one batch of scalar loads
+// before the first weight load. Otherwise segments are in row order, unused slots start at
+// INT32_MAX, and every field is picked with selects. Works for uniform and per-lane rows.
 struct RowRef {
     const uint16_t *w;
     float *y;
     int64_t ldy;
 };
 
+// A kernel-argument value known to be the same in every lane, pinned to scalar registers.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <bool MULTI>
 __device__ __forceinline__ RowRef locate(const Problem &p, int row)
 {
-    const uint16_t *w = p.seg[0].w + (int64_t)row * p.seg[0].ldw;
-    float *y = p.seg[0].y + row;
-    int64_t ldy = p.seg[0].ldy;
+    if constexpr (!MULTI)
+        return {p.w0 + (int64_t)row * p.ldw0, p.y0 + row, p.ldy0};
+    // Every field is first read as a uniform value; selecting between struct members
+    // directly is folded into an address select, which spills the by-value arguments to
+    // scratch and turns every load into a flat load.
+    uint64_t w[GEMV_MAX_SEGMENTS], y[GEMV_MAX_SEGMENTS];
+    int64_t ldw[GEMV_MAX_SEGMENTS], ldy[GEMV_MAX_SEGMENTS];
+    int row0[GEMV_MAX_SEGMENTS];
 #pragma unroll
-    for (int i = 1; i < GEMV_MAX_SEGMENTS; ++i) {
-        if (i < p.nseg && row >= p.seg[i].row0) {
-            int local = row - p.seg[i].row0;
-            w = p.seg[i].w + (int64_t)local * p.seg[i].ldw;
-            y = p.seg[i].y + local;
-            ldy = p.seg[i].ldy;
-        }
+    for (int i = 0; i < GEMV_MAX_SEGMENTS; ++i) {
+        w[i] = uniform64((uint64_t)p.seg[i].w);
+        y[i] = uniform64((uint64_t)p.seg[i].y);
+        ldw[i] = (int64_t)uniform64((uint64_t)p.seg[i].ldw);
+        ldy[i] = (int64_t)uniform64((uint64_t)p.seg[i].ldy);
+        row0[i] = __builtin_amdgcn_readfirstlane(p.seg[i].row0);
     }
-    return {w, y, ldy};
+    const int j = (row >= row0[1]) + (row >= row0[2]) + (row >= row0[3]);
+    const uint64_t wj = j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : w[3];
+    const uint64_t yj = j == 0 ? y[0] : j == 1 ? y[1] : j == 2 ? y[2] : y[3];
+    const int64_t ldwj = j == 0 ? ldw[0] : j == 1 ? ldw[1] : j == 2 ? ldw[2] : ldw[3];
+    const int64_t ldyj = j == 0 ? ldy[0] : j == 1 ? ldy[1] : j == 2 ? ldy[2] : ldy[3];
+    const int local = row - (j == 0 ? row0[0] : j == 1 ? row0[1] : j == 2 ? row0[2] : row0[3]);
+    // Pointers are rebuilt as offsets from segment 0's pointers so that they keep the
+    // global address space (a pointer made from an integer becomes a flat pointer).
+    const int64_t dw = (int64_t)(wj - w[0]) / (int64_t)sizeof(uint16_t);
+    const int64_t dy = (int64_t)(yj - y[0]) / (int64_t)sizeof(float);
+    return {p.seg[0].w + dw + (int64_t)local * ldwj, p.seg[0].y + dy + local, ldyj};
 }
 
 // Reduce R x M lane partials, then lane (r * M + m) stores output (row_first + r, m).
-template <int M, int R>
+template <int M, int R, bool MULTI>
 __device__ __forceinline__ void finish(const Problem &p, float (&acc)[R][M], int row_first,
                                        int split, int lane)
 {
@@ -173,7 +206,7 @@ __device__ __forceinline__ void finish(const Problem &p, float (&acc)[R][M], int
                 __hip_atomic_store(p.partial + ((int64_t)split * M + m) * p.n + row, out,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             } else {
-                RowRef ref = locate(p, row);
+                RowRef ref = locate<MULTI>(p, row);
                 ref.y[(int64_t)m * ref.ldy] = out;
             }
         }
@@ -190,6 +223,7 @@ __device__ __forceinline__ void finish(const Problem &p, float (&acc)[R][M], int
 // that draws the last ticket therefore finds every other slice's partials in coherent
 // memory. L2 write-back / invalidate fences are avoided on purpose: issued per workgroup
 // they cost more than the whole GEMV.
+template <bool MULTI>
 __device__ __forceinline__ void combine_if_last(const Problem &p, int m_count,
                                                 int rows_per_block)
 {
@@ -214,7 +248,7 @@ __device__ __forceinline__ void combine_if_last(const Problem &p, int m_count,
         float v = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (unsigned sl = 1; sl < gridDim.y; ++sl)
             v += __hip_atomic_load(src + sl * plane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        RowRef ref = locate(p, row);
+        RowRef ref = locate<MULTI>(p, row);
         ref.y[(int64_t)m * ref.ldy] = v;
     }
     if (threadIdx.x == 0)
@@ -238,7 +272,7 @@ constexpr int fast_waves_per_simd()
 }
 
 // One wave's R rows over its K slice (split = blockIdx.y).
-template <int M, int R, int U>
+template <int M, int R, int U, bool MULTI>
 __device__ __forceinline__ void fast_rows(const Problem &p, int row_first, int lane)
 {
     const int split = blockIdx.y;
@@ -253,7 +287,7 @@ __device__ __forceinline__ void fast_rows(const Problem &p, int row_first, int l
     for (int r = 0; r < R; ++r) {
         // Rows past N (last wave of the grid) re-read row N-1; their sums are discarded.
         int row = min(row_first + r, p.n - 1);
-        wrow[r] = locate(p, row).w + k0;
+        wrow[r] = locate<MULTI>(p, row).w + k0;
     }
     const uint16_t *xk = p.x + k0;
 
@@ -343,12 +377,13 @@ __device__ __forceinline__ void fast_rows(const Problem &p, int row_first, int l
                 acc[r][m] = fmaf(w, bf16_to_f32(xk[m * p.ldx + kk]), acc[r][m]);
         }
     }
-    finish<M, R>(p, acc, row_first, split, lane);
+    finish<M, R, MULTI>(p, acc, row_first, split, lane);
 }
 
-// W and X 16-byte aligned with leading dimensions that are multiples of 8. Waves whose
-// rows lie past N skip the row work but still take part in the split-K combine.
-template <int M, int R, int U>
+// W and X 16-byte aligned with leading dimensions that are multiples of 8. Only the SPLIT
+// instances contain the combine (and its LDS flag and barriers); every wave, including one
+// past N in the last workgroup, reaches it.
+template <int M, int R, int U, bool SPLIT, bool MULTI>
 __global__ void __launch_bounds__(512)
     __attribute__((amdgpu_waves_per_eu(1, fast_waves_per_simd<M, R, U>()))) gemv_fast(Problem p)
 {
@@ -356,10 +391,12 @@ __global__ void __launch_bounds__(512)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves = blockDim.x >> 6;
     const int row_first = (blockIdx.x * waves + wave) * R;
-    if (row_first < p.n)
-        fast_rows<M, R, U>(p, row_first, lane);
-    if (p.partial)
-        combine_if_last(p, M, waves * R);
+    // No early exit for waves past N (only in the last workgroup): their rows are clamped to
+    // N-1 and their stores skipped, which keeps the prologue free of argument-dependent
+    // branches.
+    fast_rows<M, R, U, MULTI>(p, row_first, lane);
+    if constexpr (SPLIT)
+        combine_if_last<MULTI>(p, M, waves * R);
 }
 
 // ---------------------------------------------------------------------------- unaligned
@@ -406,7 +443,7 @@ __device__ __forceinline__ u32x4 x_window(const uint16_t *xr, int k, int K, int 
     return r;
 }
 
-template <int M>
+template <int M, bool SPLIT, bool MULTI>
 __global__ void __launch_bounds__(512) gemv_unaligned(Problem p, int rows_per_wave)
 {
     const int lane = threadIdx.x & 63;
@@ -421,7 +458,7 @@ __global__ void __launch_bounds__(512) gemv_unaligned(Problem p, int rows_per_wa
         const int row = row_first + r;
         if (row >= p.n)
             break;
-        const uint16_t *wr = locate(p, row).w;
+        const uint16_t *wr = locate<MULTI>(p, row).w;
         const int h = (int)((8u - (unsigned)(((uintptr_t)wr >> 1) & 7u)) & 7u);
         const int ka = k0 + h;                        // first vector start (k0 % 8 == 0)
         const int nvec = ka + 8 <= kend ? (kend - ka) >> 3 : 0;
@@ -454,46 +491,56 @@ __global__ void __launch_bounds__(512) gemv_unaligned(Problem p, int rows_per_wa
             for (int m = 0; m < M; ++m)
                 acc[0][m] = fmaf(w, bf16_to_f32(p.x[m * p.ldx + kk]), acc[0][m]);
         }
-        finish<M, 1>(p, acc, row, split, lane);
+        finish<M, 1, MULTI>(p, acc, row, split, lane);
     }
-    if (p.partial)
-        combine_if_last(p, M, waves * rows_per_wave);
+    if constexpr (SPLIT)
+        combine_if_last<MULTI>(p, M, waves * rows_per_wave);
 }
 
 // ---------------------------------------------------------------------------- dispatch
 using FastKernel = void (*)(Problem);
 using UnalignedKernel = void (*)(Problem, int);
 
-template <size_t I>
+template <size_t I, bool SPLIT, bool MULTI>
 constexpr FastKernel fast_at()
 {
     constexpr bbd::Variant v = bbd::kVariants[I];
-    return &gemv_fast<v.m, v.r, v.u>;
+    return &gemv_fast<v.m, v.r, v.u, SPLIT, MULTI>;
 }
 
-template <size_t... I>
+template <bool SPLIT, bool MULTI, size_t... I>
 constexpr std::array<FastKernel, sizeof...(I)> fast_table(std::index_sequence<I...>)
 {
-    return {fast_at<I>()...};
+    return {fast_at<I, SPLIT, MULTI>()...};
 }
 
 constexpr size_t kNumVariants = sizeof(bbd::kVariants) / sizeof(bbd::kVariants[0]);
-const std::array<FastKernel, kNumVariants> kFast = fast_table(std::make_index_sequence<kNumVariants>{});
+using FastTable = std::array<FastKernel, kNumVariants>;
+// [split][multi]
+const FastTable kFast[2][2] = {
+    {fast_table<false, false>(std::make_index_sequence<kNumVariants>{}),
+     fast_table<false, true>(std::make_index_sequence<kNumVariants>{})},
+    {fast_table<true, false>(std::make_index_sequence<kNumVariants>{}),
+     fast_table<true, true>(std::make_index_sequence<kNumVariants>{})}};
 
-template <size_t... I>
+template <bool SPLIT, bool MULTI, size_t... I>
 constexpr std::array<UnalignedKernel, sizeof...(I)> unaligned_table(std::index_sequence<I...>)
 {
-    return {&gemv_unaligned<(int)I + 1>...};
+    return {&gemv_unaligned<(int)I + 1, SPLIT, MULTI>...};
 }
 
-const std::array<UnalignedKernel, GEMV_MAX_M> kUnaligned =
-    unaligned_table(std::make_index_sequence<GEMV_MAX_M>{});
+using UnalignedTable = std::array<UnalignedKernel, GEMV_MAX_M>;
+const UnalignedTable kUnaligned[2][2] = {
+    {unaligned_table<false, false>(std::make_index_sequence<GEMV_MAX_M>{}),
+     unaligned_table<false, true>(std::make_index_sequence<GEMV_MAX_M>{})},
+    {unaligned_table<true, false>(std::make_index_sequence<GEMV_MAX_M>{}),
+     unaligned_table<true, true>(std::make_index_sequence<GEMV_MAX_M>{})}};
 
-FastKernel find_fast(int m, int r, int u)
+FastKernel find_fast(int m, int r, int u, bool split, bool multi)
 {
     for (size_t i = 0; i < kNumVariants; ++i)
         if (bbd::kVariants[i].m == m && bbd::kVariants[i].r == r && bbd::kVariants[i].u == u)
-            return kFast[i];
+            return kFast[split][multi][i];
     return nullptr;
 }
 
@@ -549,16 +596,26 @@ gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void
 
     Problem prob = {};
     bool fast = aligned16(X) && (p->m == 1 || ldx % 8 == 0);
+    prob.w0 = static_cast<const uint16_t *>(segs[0].W);
+    prob.ldw0 = segs[0].ldw;
+    prob.y0 = segs[0].Y;
+    prob.ldy0 = segs[0].ldy;
     int64_t row0 = 0;
-    for (int i = 0; i < nseg; ++i) {
-        prob.seg[i].w = static_cast<const uint16_t *>(segs[i].W);
-        prob.seg[i].ldw = segs[i].ldw;
-        prob.seg[i].y = segs[i].Y;
-        prob.seg[i].ldy = segs[i].ldy;
-        prob.seg[i].row0 = (int32_t)row0;
-        row0 += segs[i].n;
-        fast = fast && aligned16(segs[i].W) && segs[i].ldw % 8 == 0;
+    for (int i = 0; i < GEMV_MAX_SEGMENTS; ++i) {
+        Seg &sg = prob.seg[i];
+        if (i < nseg) {
+            sg.w = static_cast<const uint16_t *>(segs[i].W);
+            sg.ldw = segs[i].ldw;
+            sg.y = segs[i].Y;
+            sg.ldy = segs[i].ldy;
+            sg.row0 = (int32_t)row0;
+            row0 += segs[i].n;
+        } else {
+            sg.row0 = INT32_MAX;            // never selected by locate()
+        }
     }
+    for (int i = 0; i < nseg; ++i)
+        fast = fast && aligned16(segs[i].W) && segs[i].ldw % 8 == 0;
     prob.nseg = nseg;
     prob.x = static_cast<const uint16_t *>(X);
     prob.ldx = p->m > 1 ? ldx : 0;
@@ -575,7 +632,7 @@ gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void
     dim3 block((unsigned)p->block_threads);
     hipError_t e;
     if (fast) {
-        FastKernel k = find_fast(p->m, p->rows_per_wave, p->unroll);
+        FastKernel k = find_fast(p->m, p->rows_per_wave, p->unroll, p->splits > 1, nseg > 1);
         if (!k)
             return GEMV_ERR_INVALID_ARG;
         void *args[] = {&prob};
@@ -583,8 +640,9 @@ gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void
     } else {
         int r = p->rows_per_wave;
         void *args[] = {&prob, &r};
-        e = hipLaunchKernel(reinterpret_cast<const void *>(kUnaligned[p->m - 1]), grid, block,
-                            args, 0, s);
+        e = hipLaunchKernel(
+            reinterpret_cast<const void *>(kUnaligned[p->splits > 1][nseg > 1][p->m - 1]), grid,
+            block, args, 0, s);
     }
     if (e != hipSuccess)
         return device_error(e);

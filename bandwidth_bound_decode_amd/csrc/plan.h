@@ -36,8 +36,8 @@ struct Variant {
 
 // The fast-path kernels gemv.hip instantiates. Keep in sync with its dispatch table.
 constexpr Variant kVariants[] = {
-    {1, 1, 2}, {1, 1, 4}, {1, 1, 8}, {1, 2, 2}, {1, 2, 4}, {1, 2, 8}, {1, 4, 2}, {1, 4, 4},
-    {1, 4, 8},
+    {1, 1, 2}, {1, 1, 4}, {1, 1, 7}, {1, 1, 8}, {1, 1, 14}, {1, 2, 2}, {1, 2, 4}, {1, 2, 7},
+    {1, 2, 8}, {1, 4, 2}, {1, 4, 4}, {1, 4, 7}, {1, 4, 8},
     {2, 1, 2}, {2, 1, 4}, {2, 2, 2}, {2, 2, 4},
     {3, 1, 2}, {3, 1, 4}, {3, 2, 2}, {3, 2, 4},
     {4, 1, 2}, {4, 1, 4}, {4, 2, 2}, {4, 2, 4},

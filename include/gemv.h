@@ -62,7 +62,8 @@ typedef struct gemv_plan_s *gemv_plan_t;
  *   rows_per_wave   R, output rows one 64-lane wave reduces together (1, 2 or 4).
  *   waves_per_block waves in a workgroup (1, 2, 4 or 8).
  *   unroll          U, independent 16-byte W loads per row each lane issues before using
- *                   any of them (cause 2 of the same section): 2, 4 or 8.
+ *                   any of them (cause 2 of the same section): 2, 4, 7, 8 or 14 (7 and 14
+ *                   divide the 28 wave steps of a 14336-element row).
  * Not every (M, R, U) combination is compiled; an unsupported one is GEMV_ERR_INVALID_ARG.
  */
 typedef struct {

@@ -175,3 +175,16 @@ def test_graph_argument_errors():
     assert lib.gemv_graph_end(None, ctypes.byref(out)) == Status.CAPTURE
     assert lib.gemv_graph_launch(None, None) == Status.INVALID_ARG
     lib.gemv_graph_destroy(None)
+
+
+def test_no_kernel_uses_scratch():
+    """The build records the compiler's per-kernel resource usage and refuses scratch or VGPR
+    spills; every kernel keeps enough occupancy for its loads in flight."""
+    import json
+    report = os.path.join(os.path.dirname(bbd.LIB_PATH), "kernel_resources.json")
+    kernels = json.load(open(report))
+    assert len(kernels) >= 2 * 2 * 13 + 2 * 2 * 16
+    for name, r in kernels.items():
+        assert r["ScratchSize [bytes/lane]"] == "0", name
+        assert r["VGPRs Spill"] == "0", name
+        assert int(r["Occupancy [waves/SIMD]"]) >= 2, name

@@ -154,7 +154,7 @@ def test_every_variant_same_bits():
         W, X = device_matrix(w), device_matrix(x)
         ref = None
         for r in (1, 2, 4):
-            for u in (2, 4, 8):
+            for u in (2, 4, 7, 8, 14):
                 for waves in (1, 4, 8):
                     try:
                         p = bbd.Plan(n, k, m, splits=2, rows_per_wave=r, unroll=u,

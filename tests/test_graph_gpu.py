@@ -48,7 +48,7 @@ def test_small_graph():
     """A short mixed sequence: split and unsplit plans, a fused call, a batch of 3."""
     drawn = []
     for i, (n, k, m, segs) in enumerate([(1024, 4096, 1, ()), (600, 4096, 1, (100, 500)),
-                                         (256, 14336, 1, ()), (4096, 14336, 1, ()),
+                                         (64, 14336, 1, ()), (4096, 14336, 1, ()),
                                          (77, 1000, 3, ())]):
         w, x = draw(n, k, m, seed=50 + i)
         parts = [device_matrix(p) for p in (torch.split(w, list(segs)) if segs else [w])]
