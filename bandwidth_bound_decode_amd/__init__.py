@@ -3,8 +3,8 @@
 The compute runs in hand-written gfx950 HIP kernels inside lib/libbbd_gemv.so (C ABI in
 include/gemv.h); this package is the thin ctypes binding over it.
 """
-from ._binding import (LIB_PATH, MAX_M, MAX_SEGMENTS, SIGNATURES, GemvError, Graph, Plan,
-                       Status, bytes_in_flight, fused_run, lib, run)
+from ._binding import (LIB_PATH, MAX_M, MAX_SEGMENTS, SIGNATURES, Chain, GemvError, Graph,
+                       Plan, Status, bytes_in_flight, fused_run, lib, run)
 
-__all__ = ["LIB_PATH", "MAX_M", "MAX_SEGMENTS", "SIGNATURES", "GemvError", "Graph", "Plan",
-           "Status", "bytes_in_flight", "fused_run", "lib", "run"]
+__all__ = ["LIB_PATH", "MAX_M", "MAX_SEGMENTS", "SIGNATURES", "Chain", "GemvError", "Graph",
+           "Plan", "Status", "bytes_in_flight", "fused_run", "lib", "run"]

@@ -27,6 +27,7 @@ class Status(enum.IntEnum):
     WORKSPACE = 3
     DEVICE = 4
     CAPTURE = 5
+    TIMEOUT = 6
 
 
 class GemvError(RuntimeError):
@@ -65,6 +66,15 @@ class Segment(ctypes.Structure):
                 ("Y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
 
 
+class ChainLink(ctypes.Structure):
+    _fields_ = [("segs", ctypes.POINTER(Segment)), ("nseg", ctypes.c_int),
+                ("X", ctypes.c_void_p), ("k", ctypes.c_int64)]
+
+
+class ChainOpts(ctypes.Structure):
+    _fields_ = [("waves_per_cu", ctypes.c_int), ("spin_limit", ctypes.c_uint)]
+
+
 # Exported symbols and their C signatures (kept in the order of include/gemv.h).
 _I64, _P, _INT, _SZ = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
@@ -81,6 +91,11 @@ SIGNATURES = {
     "gemv_graph_end": (_INT, [_P, ctypes.POINTER(_P)]),
     "gemv_graph_launch": (_INT, [_P, _P]),
     "gemv_graph_destroy": (None, [_P]),
+    "gemv_chain_create": (_INT, [ctypes.POINTER(_P), ctypes.POINTER(ChainLink), _INT, _INT,
+                                 ctypes.POINTER(ChainOpts)]),
+    "gemv_chain_run": (_INT, [_P, _P]),
+    "gemv_chain_check": (_INT, [_P]),
+    "gemv_chain_destroy": (None, [_P]),
     "gemv_status_string": (ctypes.c_char_p, [_INT]),
     "gemv_last_hip_error": (_INT, []),
 }
@@ -269,6 +284,57 @@ class Graph:
     def destroy(self):
         if self._h:
             _lib.gemv_graph_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+class Chain:
+    """Dependent batch-1 GEMVs run by one persistent launch (gemv_chain_* in gemv.h).
+
+    `links` is a list of (segments, X) with segments a list of (W, Y) pairs sharing X: link i
+    computes every Y_j = W_j . X, after link i-1 has completed. The tensors must outlive the
+    chain.
+    """
+
+    def __init__(self, links, device=None, *, waves_per_cu: int = 0, spin_limit: int = 0):
+        self._h = ctypes.c_void_p()
+        self._keep = []
+        arr = (ChainLink * len(links))()
+        for i, (segments, x) in enumerate(links):
+            segs = (Segment * len(segments))()
+            for j, (w, y) in enumerate(segments):
+                if w.dtype != torch.bfloat16 or y.dtype != torch.float32:
+                    raise TypeError("chain weights must be bfloat16 and outputs float32")
+                segs[j] = Segment(w.data_ptr(), w.shape[0], _row_stride(w, "W"), y.data_ptr(),
+                                  w.shape[0])
+            if x.dtype != torch.bfloat16:
+                raise TypeError("chain inputs must be bfloat16")
+            self._keep.append(segs)
+            arr[i] = ChainLink(segs, len(segments), x.data_ptr(), x.shape[-1])
+        if device is None:
+            device = torch.cuda.current_device()
+        idx = torch.device(device).index if not isinstance(device, int) else device
+        opts = ChainOpts(int(waves_per_cu), int(spin_limit))
+        _check(_lib.gemv_chain_create(ctypes.byref(self._h), arr, len(links), int(idx or 0),
+                                      ctypes.byref(opts)), "gemv_chain_create")
+        self._keep = None
+        self.nlinks = len(links)
+
+    def run(self, stream=None):
+        _check(_lib.gemv_chain_run(self._h, _stream_handle(stream)), "gemv_chain_run")
+
+    def check(self):
+        """Synchronise; raise GemvError(TIMEOUT) if a dependency wait of a run gave up."""
+        _check(_lib.gemv_chain_check(self._h), "gemv_chain_check")
+
+    def destroy(self):
+        if self._h:
+            _lib.gemv_chain_destroy(self._h)
             self._h = ctypes.c_void_p()
 
     def __del__(self):

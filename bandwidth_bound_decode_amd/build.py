@@ -29,6 +29,7 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror",
 
 
 RESOURCE_REPORT = os.path.join(LIB_DIR, "kernel_resources.json")
+HIP_UNITS = ("gemv", "chain")
 REMARK = "[-Rpass-analysis=kernel-resource-usage]"
 
 
@@ -77,18 +78,21 @@ def build(out: str = LIB_PATH, save_temps: str | None = None) -> str:
     os.makedirs(os.path.dirname(out), exist_ok=True)
     with tempfile.TemporaryDirectory() as tmp:
         plan_o = os.path.join(tmp, "plan.o")
-        gemv_o = os.path.join(tmp, "gemv.o")
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
-        remarks = _run([HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage",
-                        "-c", os.path.join(CSRC, "gemv.hip"), "-o", gemv_o])
-        if save_temps:
-            # the device assembly, for reading the generated code
-            os.makedirs(save_temps, exist_ok=True)
-            _run([HIPCC, *HIP_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, "gemv.hip"),
-                  "-o", os.path.join(save_temps, "gemv-hip-amdgcn-amd-amdhsa-gfx950.s")])
+        objs, remarks = [plan_o], []
+        for unit in HIP_UNITS:
+            obj = os.path.join(tmp, unit + ".o")
+            remarks += _run([HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage",
+                             "-c", os.path.join(CSRC, unit + ".hip"), "-o", obj])
+            objs.append(obj)
+            if save_temps:
+                # the device assembly, for reading the generated code
+                os.makedirs(save_temps, exist_ok=True)
+                _run([HIPCC, *HIP_FLAGS, "--cuda-device-only", "-S",
+                      os.path.join(CSRC, unit + ".hip"),
+                      "-o", os.path.join(save_temps, f"{unit}-hip-amdgcn-amd-amdhsa-gfx950.s")])
         tmp_out = out + ".tmp"
-        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", plan_o, gemv_o,
-              "-o", tmp_out])
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_out])
         kernels = _resources(remarks)
         _check_resources(kernels)
         os.replace(tmp_out, out)

@@ -34,12 +34,12 @@
 #include <array>
 #include <utility>
 
+#include "device.h"
 #include "plan.h"
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+using namespace bbd;
 
 struct Seg {
     const uint16_t *w;  // row 0 of the segment's weight
@@ -68,67 +68,6 @@ struct Problem {
     float *partial;     // [S][M][N] when the plan splits K, else null
     unsigned *tickets;  // [grid_x] arrival counters, zero between calls (split plans only)
 };
-
-// ---------------------------------------------------------------------------- helpers
-
-// Element access goes through by-value scalars: clang mis-lowers __builtin_bit_cast
-// applied directly to an ext_vector element (it reads element 0).
-__device__ __forceinline__ float dot2(unsigned w, unsigned x, float acc)
-{
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
-                                           __builtin_bit_cast(bf16x2, x), acc, false);
-}
-
-__device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc)
-{
-    unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
-    unsigned x0 = x.x, x1 = x.y, x2 = x.z, x3 = x.w;
-    acc = dot2(w0, x0, acc);
-    acc = dot2(w1, x1, acc);
-    acc = dot2(w2, x2, acc);
-    acc = dot2(w3, x3, acc);
-    return acc;
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b)
-{
-    return __uint_as_float((unsigned)b << 16);
-}
-
-__device__ __forceinline__ u32x4 load_stream(const uint16_t *p)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-
-__device__ __forceinline__ u32x4 load_cached(const uint16_t *p)
-{
-    return *reinterpret_cast<const u32x4 *>(p);
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp(float v)
-{
-    // Lanes outside ROW_MASK keep `old` = 0, so adding the result leaves them unchanged.
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK,
-                                                      0xF, false));
-}
-
-// Sum of the 64 lane values, valid in lane 63. Fixed tree, hence deterministic.
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v += dpp<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]: pairs
-    v += dpp<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]: quads
-    v += dpp<0x141, 0xF>(v);  // row_half_mirror: 8 lanes
-    v += dpp<0x140, 0xF>(v);  // row_mirror: 16 lanes (a full DPP row)
-    v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-    v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-    return v;
-}
-
-__device__ __forceinline__ float lane63(float v)
-{
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
 
 // Segment holding global row `row`. The single-segment instances (MULTI = false, every
 // gemv_run) read only the argument header, so their prologue is one batch of scalar loads
@@ -544,13 +483,7 @@ FastKernel find_fast(int m, int r, int u, bool split, bool multi)
     return nullptr;
 }
 
-thread_local int g_last_hip_error = 0;
-
-gemv_status device_error(hipError_t e)
-{
-    g_last_hip_error = (int)e;
-    return GEMV_ERR_DEVICE;
-}
+gemv_status device_error(hipError_t e) { return record_hip_error((int)e, GEMV_ERR_DEVICE); }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
@@ -668,10 +601,8 @@ extern "C" gemv_status gemv_plan(gemv_plan_t *out, int64_t n, int64_t k, int m, 
     hipError_t e = hipGetDeviceProperties(&prop, device);
     if (e != hipSuccess)
         return device_error(e);
-    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
-        g_last_hip_error = 0;
-        return GEMV_ERR_DEVICE;
-    }
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return record_hip_error(0, GEMV_ERR_DEVICE);
     // MI355X: 8.0 TB/s HBM3E (published peak); the plan uses it only to report Little's law.
     gemv_device_desc dev = {prop.multiProcessorCount, 8.0e12, bbd::kDefaultLatency};
     gemv_status st = gemv_plan_for(out, n, k, m, &dev, opts);
@@ -703,10 +634,8 @@ extern "C" gemv_status gemv_graph_begin(void *stream)
         return GEMV_ERR_CAPTURE;
     hipError_t e = hipStreamBeginCapture(static_cast<hipStream_t>(stream),
                                          hipStreamCaptureModeThreadLocal);
-    if (e != hipSuccess) {
-        g_last_hip_error = (int)e;
-        return GEMV_ERR_CAPTURE;
-    }
+    if (e != hipSuccess)
+        return record_hip_error((int)e, GEMV_ERR_CAPTURE);
     return GEMV_OK;
 }
 
@@ -719,10 +648,8 @@ extern "C" gemv_status gemv_graph_end(void *stream, gemv_graph_t *out)
         return GEMV_ERR_CAPTURE;
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamEndCapture(static_cast<hipStream_t>(stream), &graph);
-    if (e != hipSuccess || !graph) {
-        g_last_hip_error = (int)e;
-        return GEMV_ERR_CAPTURE;
-    }
+    if (e != hipSuccess || !graph)
+        return record_hip_error((int)e, GEMV_ERR_CAPTURE);
     hipGraphExec_t exec = nullptr;
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     if (e != hipSuccess) {
@@ -758,4 +685,18 @@ extern "C" void gemv_graph_destroy(gemv_graph_t g)
     delete g;
 }
 
-extern "C" int gemv_last_hip_error(void) { return g_last_hip_error; }
+namespace bbd {
+
+namespace {
+thread_local int g_last_hip_error = 0;
+}
+
+gemv_status record_hip_error(int hip_error, gemv_status status)
+{
+    g_last_hip_error = hip_error;
+    return status;
+}
+
+}  // namespace bbd
+
+extern "C" int gemv_last_hip_error(void) { return bbd::g_last_hip_error; }

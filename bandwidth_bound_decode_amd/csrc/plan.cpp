@@ -241,6 +241,7 @@ extern "C" const char *gemv_status_string(gemv_status s)
     case GEMV_ERR_WORKSPACE: return "workspace missing or too small";
     case GEMV_ERR_DEVICE: return "device error or unsupported device";
     case GEMV_ERR_CAPTURE: return "graph capture error";
+    case GEMV_ERR_TIMEOUT: return "chain dependency wait exceeded its spin limit";
     }
     return "unknown status";
 }

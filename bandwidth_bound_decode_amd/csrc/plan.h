@@ -49,6 +49,10 @@ constexpr Variant kVariants[] = {
 
 bool variant_supported(int m, int r, int u);
 
+// Record the HIP error code behind a GEMV_ERR_DEVICE / GEMV_ERR_CAPTURE for
+// gemv_last_hip_error() (thread-local) and return `status`.
+gemv_status record_hip_error(int hip_error, gemv_status status);
+
 }  // namespace bbd
 
 struct gemv_plan_s {

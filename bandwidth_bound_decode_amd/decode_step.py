@@ -1,4 +1,5 @@
-"""A decode step's GEMV sequence, run eagerly or replayed from one captured graph.
+"""A decode step's GEMV sequence, run eagerly, replayed from one captured graph, or run as
+one persistent chain launch.
 
 The sequence is a list of calls, each one weight matrix (or several that share X: the fused
 QKV and gate_up projections), one input X and its outputs. Calls run in list order on one
@@ -16,7 +17,7 @@ from dataclasses import dataclass
 
 import torch
 
-from ._binding import Graph, Plan, fused_run, run
+from ._binding import Chain, Graph, Plan, fused_run, run
 
 
 @dataclass
@@ -63,6 +64,11 @@ class Sequence:
 
     def replay(self, stream=None):
         self.graph.launch(stream)
+
+    def chain(self, **opts) -> Chain:
+        """The same sequence as one persistent launch (batch-1 calls only): every call waits
+        for the previous one to complete, but streams its weights ahead of that wait."""
+        return Chain([(list(zip(c.weights, c.ys)), c.x) for c in self.calls], **opts)
 
     @property
     def weight_bytes(self) -> int:

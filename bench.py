@@ -190,6 +190,8 @@ def bench_gemv(torch, bbd, g, w, x, steps, warmup, segments=(), **plan_opts):
 
 
 def bench_decode_step(torch, bbd, workloads, replays, warmup):
+    """The 129-GEMV decode step three ways: eager launches, one graph of the 129 launches,
+    and one graph holding the single persistent chain launch."""
     from bandwidth_bound_decode_amd.decode_step import Call, Sequence
     drawn = workloads.draw_decode_step("cuda")
     calls = [Call(parts, x, [torch.empty((x.shape[0], w.shape[0]), device="cuda")
@@ -197,20 +199,35 @@ def bench_decode_step(torch, bbd, workloads, replays, warmup):
     seq = Sequence(calls)
     nb = seq.alg_bytes
     stream = torch.cuda.Stream()
+    chain = seq.chain()
     with torch.cuda.stream(stream):
-        eager_total, eager_per = time_launches(torch, lambda i: seq.run(stream), replays, warmup,
-                                               stream)
+        _, eager_per = time_launches(torch, lambda i: seq.run(stream), replays, warmup, stream)
         seq.capture(stream)
-        graph_total, graph_per = time_launches(torch, lambda i: seq.replay(stream), replays,
-                                               warmup, stream)
-    t_graph = statistics.median(graph_per)
-    t_eager = statistics.median(eager_per)
+        _, graph_per = time_launches(torch, lambda i: seq.replay(stream), replays, warmup,
+                                     stream)
+        cg = bbd.Graph(stream)
+        with cg:
+            chain.run(stream)
+        _, chain_per = time_launches(torch, lambda i: cg.launch(stream), replays, warmup,
+                                     stream)
+    chain.check()
     out = {"gemvs": len(calls), "alg_bytes": nb, "weight_bytes": seq.weight_bytes,
-           "replays": replays, "graph_ms_median": t_graph * 1e3,
-           "graph_ms_p10": pct(graph_per, 0.1) * 1e3, "graph_ms_p90": pct(graph_per, 0.9) * 1e3,
-           "graph_TBps": nb / t_graph / 1e12, "graph_mbu": mbu(nb, t_graph, PEAK_HBM),
-           "eager_ms_median": t_eager * 1e3, "eager_mbu": mbu(nb, t_eager, PEAK_HBM),
-           "gate_fraction": 0.80, "meets_gate": mbu(nb, t_graph, PEAK_HBM) >= 0.80}
+           "replays": replays}
+    for name, per in (("eager", eager_per), ("graph", graph_per), ("chain_graph", chain_per)):
+        t = statistics.median(per)
+        out[f"{name}_ms_median"] = t * 1e3
+        out[f"{name}_ms_p10"] = pct(per, 0.1) * 1e3
+        out[f"{name}_ms_p90"] = pct(per, 0.9) * 1e3
+        out[f"{name}_TBps"] = nb / t / 1e12
+        out[f"{name}_mbu"] = mbu(nb, t, PEAK_HBM)
+    out["gate_fraction"] = 0.80
+    out["meets_gate"] = out["chain_graph_mbu"] >= 0.80 or out["graph_mbu"] >= 0.80
+    out["note"] = ("graph: one hipGraph of the 129 GEMV launches (fused QKV and gate_up); "
+                   "chain_graph: one hipGraph holding a single persistent launch that runs "
+                   "the 129 GEMVs in order, each waiting for the previous one to complete "
+                   "while its weights already stream")
+    cg.destroy()
+    chain.destroy()
     seq.graph.destroy()
     del seq, calls, drawn
     torch.cuda.empty_cache()
@@ -355,8 +372,10 @@ def main(argv=None):
             if isinstance(d[k], float):
                 d[k] = round(d[k], 4)
         out["decode_step"] = d
-        log(f"decode step: graph {d['graph_ms_median']:.3f} ms (MBU {d['graph_mbu']:.3f}), "
-            f"eager {d['eager_ms_median']:.3f} ms")
+        log(f"decode step: chain in a graph {d['chain_graph_ms_median']:.3f} ms "
+            f"(MBU {d['chain_graph_mbu']:.3f}); graph of 129 launches "
+            f"{d['graph_ms_median']:.3f} ms (MBU {d['graph_mbu']:.3f}); eager "
+            f"{d['eager_ms_median']:.3f} ms")
 
     print(json.dumps(out), flush=True)
     return 0

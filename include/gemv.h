@@ -45,7 +45,8 @@ typedef enum {
     GEMV_ERR_MISALIGNED = 2,  /* W/X not 2-byte aligned, or Y/workspace not 4-byte aligned */
     GEMV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than gemv_workspace_size()   */
     GEMV_ERR_DEVICE = 4,      /* not a gfx950 device, or a HIP call failed                  */
-    GEMV_ERR_CAPTURE = 5      /* graph capture misuse (legacy stream, not capturing, ...)   */
+    GEMV_ERR_CAPTURE = 5,     /* graph capture misuse (legacy stream, not capturing, ...)   */
+    GEMV_ERR_TIMEOUT = 6      /* a chain's dependency wait exceeded its spin limit          */
 } gemv_status;
 
 /* Largest batch a plan accepts (the skinny-batch range of the decode-GEMV page). */
@@ -191,6 +192,60 @@ gemv_status gemv_graph_begin(void *stream);
 gemv_status gemv_graph_end(void *stream, gemv_graph_t *out);
 gemv_status gemv_graph_launch(gemv_graph_t g, void *stream);
 void gemv_graph_destroy(gemv_graph_t g);
+
+/*
+ * A chain: a decode step's dependent GEMVs run by ONE persistent launch (decode-GEMV page,
+ * "A strong answer", cause 3: launch and ramp-up cost rivals the transfer of a small
+ * matrix; GPU performance chains page, "Launch gaps in a decode step").
+ *
+ * Link i is one GEMV (batch 1) whose input may be the previous link's output: no wave
+ * computes with link i's input before every output of link i-1 has been stored and made
+ * visible device-wide. Waves issue the first weight loads of their next link before they
+ * wait for that dependency, because weights never depend on the previous result - so HBM
+ * keeps streaming across link boundaries instead of draining and refilling once per GEMV.
+ * Each output row is summed exactly as gemv_run / gemv_fused_run sum it with an unsplit
+ * plan, so a chain's results are bitwise equal to running its links one by one.
+ *
+ * Every dependency wait is bounded by a spin limit; a wait that runs out sets an error flag
+ * and the launch finishes early (never hangs). gemv_chain_check reports it.
+ */
+typedef struct {
+    const gemv_segment *segs;   /* 1..GEMV_MAX_SEGMENTS weights and outputs sharing X; the
+                                   segment ldy fields are ignored (batch 1) */
+    int nseg;
+    const void *X;              /* bf16 [k], 16-byte aligned */
+    int64_t k;                  /* reduction length of every segment */
+} gemv_chain_link;
+
+typedef struct {
+    int waves_per_cu;           /* persistent waves per CU (0 = auto) */
+    unsigned spin_limit;        /* polls before a dependency wait gives up (0 = auto, ~1 s) */
+} gemv_chain_opts;
+
+typedef struct gemv_chain_s *gemv_chain_t;
+
+/*
+ * Build a chain on HIP device `device` from `nlinks` >= 1 links (read during the call only).
+ * Every weight must be 16-byte aligned with ldw a multiple of 8 and every X 16-byte aligned
+ * (the fast-path layout; anything else is GEMV_ERR_MISALIGNED). Allocates the chain's
+ * device-side descriptor table and counters here, once; gemv_chain_run allocates nothing.
+ * The weights, inputs and outputs stay owned by the caller and must outlive the chain.
+ */
+gemv_status gemv_chain_create(gemv_chain_t *out, const gemv_chain_link *links, int nlinks,
+                              int device, const gemv_chain_opts *opts);
+
+/* One launch that runs every link in order on `stream`; asynchronous and capturable. */
+gemv_status gemv_chain_run(gemv_chain_t c, void *stream);
+
+/*
+ * Synchronise with the device and report GEMV_ERR_TIMEOUT if a dependency wait of an
+ * earlier run gave up (that run's outputs are then incomplete); clears the flag. Not for
+ * use during graph capture.
+ */
+gemv_status gemv_chain_check(gemv_chain_t c);
+
+/* Release a chain and its device memory (NULL is allowed). */
+void gemv_chain_destroy(gemv_chain_t c);
 
 /* A static description of a status code ("unknown status" for anything else). */
 const char *gemv_status_string(gemv_status s);

@@ -188,3 +188,33 @@ def test_no_kernel_uses_scratch():
         assert r["ScratchSize [bytes/lane]"] == "0", name
         assert r["VGPRs Spill"] == "0", name
         assert int(r["Occupancy [waves/SIMD]"]) >= 2, name
+
+
+def test_chain_validation_before_any_hip_call():
+    from bandwidth_bound_decode_amd._binding import ChainLink
+    lib = bbd.lib()
+    h = ctypes.c_void_p()
+
+    def create(links, n=None):
+        arr = (ChainLink * max(len(links), 1))(*links)
+        return lib.gemv_chain_create(ctypes.byref(h), arr, len(links) if n is None else n, 0,
+                                     None)
+
+    seg = (Segment * 2)(Segment(FAKE, 64, 4096, FAKE, 64), Segment(FAKE, 32, 4096, FAKE, 32))
+    good = ChainLink(seg, 2, FAKE, 4096)
+    assert lib.gemv_chain_create(None, None, 1, 0, None) == Status.INVALID_ARG
+    assert create([good], n=0) == Status.INVALID_ARG
+    assert create([ChainLink(seg, 0, FAKE, 4096)]) == Status.INVALID_ARG
+    assert create([ChainLink(seg, 5, FAKE, 4096)]) == Status.INVALID_ARG
+    assert create([ChainLink(seg, 2, None, 4096)]) == Status.INVALID_ARG
+    assert create([ChainLink(seg, 2, FAKE, 0)]) == Status.INVALID_ARG
+    assert create([ChainLink(seg, 2, FAKE, 4097)]) == Status.INVALID_ARG       # ldw < k
+    assert create([ChainLink(seg, 2, FAKE + 8, 4096)]) == Status.MISALIGNED    # X
+    bad_w = (Segment * 1)(Segment(FAKE + 2, 64, 4096, FAKE, 64))
+    assert create([ChainLink(bad_w, 1, FAKE, 4096)]) == Status.MISALIGNED
+    bad_ld = (Segment * 1)(Segment(FAKE, 64, 4100, FAKE, 64))
+    assert create([ChainLink(bad_ld, 1, FAKE, 4096)]) == Status.MISALIGNED
+    assert not h
+    assert lib.gemv_chain_run(None, None) == Status.INVALID_ARG
+    assert lib.gemv_chain_check(None) == Status.INVALID_ARG
+    lib.gemv_chain_destroy(None)

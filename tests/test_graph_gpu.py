@@ -68,6 +68,17 @@ def test_decode_step_full():
           flush=True)
     assert len(seq.calls) == 129
     eager = replay_matches_eager(seq, replays=2)
+    # the same step as one persistent chain launch, bitwise equal to the eager sequence
+    chain = seq.chain()
+    for rep in range(2):
+        for c in seq.calls:
+            for y in c.ys:
+                y.fill_(float("nan"))
+        chain.run()
+        chain.check()
+        for i, (a, b) in enumerate(zip(snapshot(seq), eager)):
+            assert bits_equal(a, b), f"chain run {rep}: call {i} differs from eager"
+    chain.destroy()
     rng = np.random.default_rng(4)
     for i, ((g, parts, x), y) in enumerate(zip(drawn, eager)):
         n = g.n
