@@ -200,26 +200,31 @@ void gemv_graph_destroy(gemv_graph_t g);
  *
  * Link i is one GEMV (batch 1) whose input may be the previous link's output: no wave
  * computes with link i's input before every output of link i-1 has been stored and made
- * visible device-wide. Waves issue the first weight loads of their next link before they
- * wait for that dependency, because weights never depend on the previous result - so HBM
- * keeps streaming across link boundaries instead of draining and refilling once per GEMV.
+ * visible device-wide. The launch is one workgroup per CU: worker waves stream weights and
+ * keep several bursts of loads in flight across link boundaries (weights never depend on
+ * the previous result), and one controller wave per workgroup stages x into LDS, writes the
+ * workgroup's outputs and takes part in the grid-wide wait between links - so HBM keeps
+ * streaming across link boundaries instead of draining and refilling once per GEMV.
  * Each output row is summed exactly as gemv_run / gemv_fused_run sum it with an unsplit
  * plan, so a chain's results are bitwise equal to running its links one by one.
  *
- * Every dependency wait is bounded by a spin limit; a wait that runs out sets an error flag
- * and the launch finishes early (never hangs). gemv_chain_check reports it.
+ * Every wait is bounded by a spin limit; a wait that runs out sets an error flag and the
+ * launch finishes early (never hangs). gemv_chain_check reports it. Two runs of one chain
+ * must not execute concurrently (they share its counters); runs on one stream never do.
  */
 typedef struct {
     const gemv_segment *segs;   /* 1..GEMV_MAX_SEGMENTS weights and outputs sharing X; the
                                    segment ldy fields are ignored (batch 1) */
     int nseg;
     const void *X;              /* bf16 [k], 16-byte aligned */
-    int64_t k;                  /* reduction length of every segment */
+    int64_t k;                  /* reduction length of every segment, >= 8; x of the
+                                   longest link must fit in one CU's LDS (k up to ~80K) */
 } gemv_chain_link;
 
 typedef struct {
-    int waves_per_cu;           /* persistent waves per CU (0 = auto) */
-    unsigned spin_limit;        /* polls before a dependency wait gives up (0 = auto, ~1 s) */
+    int waves_per_cu;           /* worker waves per CU, 1..11 (0 = 8); one controller wave
+                                   per CU comes on top */
+    unsigned spin_limit;        /* polls before a wait gives up (0 = auto, ~1 s) */
 } gemv_chain_opts;
 
 typedef struct gemv_chain_s *gemv_chain_t;

@@ -208,12 +208,17 @@ def test_chain_validation_before_any_hip_call():
     assert create([ChainLink(seg, 5, FAKE, 4096)]) == Status.INVALID_ARG
     assert create([ChainLink(seg, 2, None, 4096)]) == Status.INVALID_ARG
     assert create([ChainLink(seg, 2, FAKE, 0)]) == Status.INVALID_ARG
+    assert create([ChainLink(seg, 2, FAKE, 7)]) == Status.INVALID_ARG          # k < 8
     assert create([ChainLink(seg, 2, FAKE, 4097)]) == Status.INVALID_ARG       # ldw < k
     assert create([ChainLink(seg, 2, FAKE + 8, 4096)]) == Status.MISALIGNED    # X
     bad_w = (Segment * 1)(Segment(FAKE + 2, 64, 4096, FAKE, 64))
     assert create([ChainLink(bad_w, 1, FAKE, 4096)]) == Status.MISALIGNED
     bad_ld = (Segment * 1)(Segment(FAKE, 64, 4100, FAKE, 64))
     assert create([ChainLink(bad_ld, 1, FAKE, 4096)]) == Status.MISALIGNED
+    from bandwidth_bound_decode_amd._binding import ChainOpts
+    for waves in (-1, 12):                                                      # 1..11 workers
+        assert lib.gemv_chain_create(ctypes.byref(h), (ChainLink * 1)(good), 1, 0,
+                                     ctypes.byref(ChainOpts(waves, 0))) == Status.INVALID_ARG
     assert not h
     assert lib.gemv_chain_run(None, None) == Status.INVALID_ARG
     assert lib.gemv_chain_check(None) == Status.INVALID_ARG

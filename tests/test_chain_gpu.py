@@ -9,9 +9,12 @@ from gpu_helpers import bits_equal, device_matrix, draw, oracle_check, output
 
 pytestmark = pytest.mark.gpu
 
-# (segment rows, K, ldw): single and fused links, both tiles, ragged K with padded rows
+# (segment rows, K, ldw): single and fused links, one- and two-row items (2049 rows give an
+# odd row count to two-row items), partial bursts, ragged K with padded rows (K = 4099: the
+# k % 8 last elements lie past every wave step a burst reads)
 LINKS = [((1024,), 4096, 4096), ((100, 500), 4096, 4096), ((4096,), 14336, 14336),
-         ((64,), 14336, 14336), ((33,), 1000, 1008), ((7,), 129, 136), ((5, 3, 2, 9), 520, 520)]
+         ((64,), 14336, 14336), ((2049,), 14336, 14336), ((33,), 1000, 1008),
+         ((7,), 129, 136), ((5, 3, 2, 9), 520, 520), ((300,), 4099, 4104)]
 
 
 def build_links(seed=0):
@@ -66,7 +69,7 @@ def test_chain_matches_links_one_by_one():
         oracle_check(torch.cat([w for w, _ in segs], 0), x, y, "chain link")
 
 
-@pytest.mark.parametrize("waves_per_cu", [1, 3, 16])
+@pytest.mark.parametrize("waves_per_cu", [1, 3, 11])
 def test_chain_grid_sizes_give_same_bits(waves_per_cu):
     links = build_links(seed=100)
     ref = one_by_one(links)
