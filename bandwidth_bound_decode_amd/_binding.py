@@ -41,7 +41,8 @@ class GemvError(RuntimeError):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
-                ("waves_per_block", ctypes.c_int), ("unroll", ctypes.c_int)]
+                ("waves_per_block", ctypes.c_int), ("unroll", ctypes.c_int),
+                ("waves_per_cu", ctypes.c_int)]
 
 
 class DeviceDesc(ctypes.Structure):
@@ -55,7 +56,8 @@ class PlanInfo(ctypes.Structure):
                 ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int),
                 ("block_threads", ctypes.c_int), ("slice", ctypes.c_int64),
                 ("depth_bound", ctypes.c_int), ("bytes_in_flight_per_cu", ctypes.c_double),
-                ("bytes_in_flight_needed", ctypes.c_double)]
+                ("bytes_in_flight_needed", ctypes.c_double), ("waves_per_cu", ctypes.c_int),
+                ("lds_bytes", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -129,8 +131,9 @@ def bytes_in_flight(bytes_per_s: float, latency_s: float) -> float:
     return float(_lib.gemv_bytes_in_flight(bytes_per_s, latency_s))
 
 
-def _opts(splits, rows_per_wave, waves_per_block, unroll):
-    return PlanOpts(int(splits), int(rows_per_wave), int(waves_per_block), int(unroll))
+def _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu=0):
+    return PlanOpts(int(splits), int(rows_per_wave), int(waves_per_block), int(unroll),
+                    int(waves_per_cu))
 
 
 class Plan:
@@ -142,9 +145,9 @@ class Plan:
 
     def __init__(self, n: int, k: int, m: int = 1, device=None, *, splits: int = 0,
                  rows_per_wave: int = 0, waves_per_block: int = 0, unroll: int = 0,
-                 desc: tuple | None = None):
+                 waves_per_cu: int = 0, desc: tuple | None = None):
         self._h = ctypes.c_void_p()
-        opts = _opts(splits, rows_per_wave, waves_per_block, unroll)
+        opts = _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu)
         if desc is not None:
             d = DeviceDesc(int(desc[0]), float(desc[1]), float(desc[2]))
             st = _lib.gemv_plan_for(ctypes.byref(self._h), n, k, m, ctypes.byref(d),

@@ -41,24 +41,27 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 // Default tile per batch size and shape: (rows per wave R, unroll U, waves per workgroup).
-// At M = 1 every wave keeps R x U = 8 loads (8 KiB) in flight. A row of up to 8 wave steps
-// (K <= 4096) is fetched by one single-row wave in one burst; longer rows go two per wave in
-// bursts of 4 when N leaves at least 8 such waves per CU (fewer, fuller waves and half the x
-// traffic), else one per wave in bursts of 8. Larger M spends VGPRs on X vectors and
-// accumulators, so the W unroll shrinks. Chosen from measured sweeps on MI355X; every choice
-// gives bitwise the same result.
+// At M = 1 every wave owns one row (measured on MI355X: single-row waves beat two- and
+// four-row waves at every Llama-8B shape once the resident-wave cap below is applied).
+//   - Rows of more than 8 wave steps (K > 4096) are read in bursts of 4 steps.
+//   - Shorter rows are read in one burst when the grid needs more than one round of
+//     waves, and in bursts of up to 4 steps when it fits in one round.
+// Larger M spends VGPRs on X vectors and accumulators, so the W unroll shrinks. Every
+// choice gives bitwise the same result.
 void default_tile(int m, int64_t n, int64_t k, int cus, int *r, int *u, int *waves)
 {
     int64_t steps = (k + kWaveStep - 1) / kWaveStep;
     if (m == 1) {
-        if (steps > 8 && n >= (int64_t)8 * 2 * cus) {
-            *r = 2;
-            *u = 4;
-        } else {
-            *r = 1;
-            *u = 8;
-        }
+        *r = 1;
         *waves = 1;
+        if (steps > 8)
+            *u = 4;
+        else if (steps <= 2)
+            *u = 2;
+        else if (steps <= 4 || n <= (int64_t)kOneRoundWavesPerCU * cus)
+            *u = 4;
+        else
+            *u = 8;
     } else if (m <= 4) {
         *r = 2;
         *u = 4;
@@ -68,6 +71,43 @@ void default_tile(int m, int64_t n, int64_t k, int cus, int *r, int *u, int *wav
         *u = 2;
         *waves = 4;
     }
+}
+
+// Automatic resident-wave cap per CU (0: none) for a batch-1 unsplit launch of `waves_total`
+// single-wave workgroups. Measured on MI355X (down_proj 4096 x 14336: 18.36 us capped at 8
+// in two equal rounds, 18.97 us uncapped in one round of 16, 20.1 us at 12 in unequal
+// rounds; gate_up, QKV and the LM head: best near 12). A cap makes the workgroups of later
+// rounds start wherever a CU frees up, which evens out the finish times of the CUs; the cap
+// is spread so that all rounds are equally full.
+int auto_cap(int m, int s, int64_t k, int64_t waves_total, int cus)
+{
+    if (m != 1 || s != 1)
+        return 0;
+    const int64_t steps = (k + kWaveStep - 1) / kWaveStep;
+    const int64_t per_cu = ceil_div(waves_total, cus);
+    int limit;
+    if (steps > 8)
+        limit = kCapLongRows;
+    else if (per_cu > kOneRoundWavesPerCU)
+        limit = kCapShortRows;
+    else
+        return 0;
+    if (per_cu <= limit)
+        return 0;
+    const int64_t rounds = ceil_div(per_cu, limit);
+    return (int)ceil_div(per_cu, rounds);
+}
+
+// LDS bytes per workgroup that let at most `blocks` workgroups share one CU's LDS, with
+// allocations in units of `granule` bytes; 0 if no such size exists.
+int lds_for_blocks(int blocks, int granule)
+{
+    if (blocks < 1)
+        return 0;
+    const int bytes = kLdsPerCU / blocks / granule * granule;
+    if (bytes < granule || (int64_t)(blocks + 1) * bytes <= kLdsPerCU)
+        return 0;
+    return bytes;
 }
 
 // K elements per split for S splits: wave-step aligned when a slice spans more than one
@@ -110,10 +150,11 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     // Row indices and grid sizes are held in 32 bits on the device.
     if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30)
         return GEMV_ERR_INVALID_ARG;
-    gemv_plan_opts o = {0, 0, 0, 0};
+    gemv_plan_opts o = {0, 0, 0, 0, 0};
     if (opts)
         o = *opts;
-    if (o.splits < 0 || o.rows_per_wave < 0 || o.waves_per_block < 0 || o.unroll < 0)
+    if (o.splits < 0 || o.rows_per_wave < 0 || o.waves_per_block < 0 || o.unroll < 0 ||
+        o.waves_per_cu < -1 || o.waves_per_cu > kMaxWavesPerCU)
         return GEMV_ERR_INVALID_ARG;
 
     int r, u, waves;
@@ -174,6 +215,24 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
             return GEMV_ERR_INVALID_ARG;
     }
 
+    // Resident-wave cap, enforced per workgroup: a whole number of workgroups per CU.
+    int cap_blocks = 0, cap_lds = 0;
+    {
+        const int64_t total = ceil_div(n, (int64_t)r * waves) * s * waves;
+        const int cap = o.waves_per_cu > 0   ? o.waves_per_cu
+                        : o.waves_per_cu < 0 ? 0
+                                             : auto_cap(m, s, k, total, dev->compute_units);
+        if (cap > 0) {
+            cap_blocks = cap / waves;
+            cap_lds = lds_for_blocks(cap_blocks, kLdsGranule);
+            if (!cap_lds) {
+                if (o.waves_per_cu > 0)   // a forced cap that cannot be enforced
+                    return GEMV_ERR_INVALID_ARG;
+                cap_blocks = 0;
+            }
+        }
+    }
+
     gemv_plan_s *p = new (std::nothrow) gemv_plan_s;
     if (!p)
         return GEMV_ERR_INVALID_ARG;
@@ -201,9 +260,13 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     }
 
     int64_t total_waves = (int64_t)p->grid_x * p->grid_y * waves;
+    p->waves_per_cu = cap_blocks * waves;
+    p->lds_bytes = cap_lds;
     int64_t per_cu = ceil_div(total_waves, dev->compute_units);
     if (per_cu > kMaxWavesPerCU)
         per_cu = kMaxWavesPerCU;
+    if (p->waves_per_cu && per_cu > p->waves_per_cu)
+        per_cu = p->waves_per_cu;
     p->bif_per_cu = (double)per_cu * u * r * kWaveLanes * 16.0;
     p->bif_needed = gemv_bytes_in_flight(dev->hbm_bytes_per_s, dev->latency_s) / dev->compute_units;
     *out = p;
@@ -227,6 +290,8 @@ extern "C" gemv_status gemv_plan_query(gemv_plan_t p, gemv_plan_info *info)
     info->depth_bound = p->depth_bound;
     info->bytes_in_flight_per_cu = p->bif_per_cu;
     info->bytes_in_flight_needed = p->bif_needed;
+    info->waves_per_cu = p->waves_per_cu;
+    info->lds_bytes = p->lds_bytes;
     return GEMV_OK;
 }
 

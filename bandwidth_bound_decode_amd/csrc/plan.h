@@ -16,6 +16,8 @@ constexpr int kVecElems = 8;            // bf16 elements per 16-byte load
 constexpr int kWaveStep = kWaveLanes * kVecElems;   // K elements one wave-wide load covers
 constexpr int kMaxWavesPerCU = 32;      // 4 SIMDs x 8 waves
 constexpr int kMaxSplits = 64;
+constexpr int kLdsPerCU = 160 * 1024;   // LDS bytes per CU
+constexpr int kLdsGranule = 512;        // LDS allocation unit assumed when planning offline
 
 // Planning constants (tunable, see the plan rule in plan.cpp).
 constexpr int kMinWavesPerCU = 1;       // no split while N / R gives this many waves per CU
@@ -23,6 +25,13 @@ constexpr int kTargetWavesPerCU = 4;    // a split aims for this many waves per 
 constexpr int64_t kMinSlice = 1024;     // never split K finer than this many elements
 constexpr int kMaxDepth = 160;          // gamma_160 (u = 2^-24) = 9.54e-6 < 1e-5
 constexpr double kDefaultLatency = 1.0e-6;   // assumed loaded HBM latency on MI355X
+// Batch-1 resident-wave caps per CU (measured on MI355X, see the plan rule in plan.cpp):
+// rows longer than 8 wave steps stream best with at most 8 single-row waves per CU, in
+// equal rounds; short rows with more waves than one round holds, with at most 12.
+constexpr int kCapLongRows = 8;
+constexpr int kCapShortRows = 12;
+constexpr int kOneRoundWavesPerCU = 16;   // short rows: up to this many waves per CU run
+                                          // as one round, uncapped
 // Ticket counters sit at the start of a split plan's workspace in a region of at least this
 // many slots, so that plans with up to this many row blocks can share one workspace in any
 // order without one plan's partial sums landing on another plan's tickets.
@@ -70,4 +79,6 @@ struct gemv_plan_s {
     size_t workspace;           // ticket counters, then the split partials
     size_t partial_offset;      // byte offset of the partial sums in the workspace
     double bif_per_cu, bif_needed;
+    int waves_per_cu;           // resident-wave cap per CU (0: none)
+    int lds_bytes;              // LDS reserved per workgroup to enforce the cap
 };

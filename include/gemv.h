@@ -65,6 +65,10 @@ typedef struct gemv_plan_s *gemv_plan_t;
  *   unroll          U, independent 16-byte W loads per row each lane issues before using
  *                   any of them (cause 2 of the same section): 2, 4, 7, 8 or 14 (7 and 14
  *                   divide the 28 wave steps of a 14336-element row).
+ *   waves_per_cu    most waves of the launch resident on one CU at a time: 1..32, or -1
+ *                   for no cap. A cap below what registers allow makes later workgroups
+ *                   start as earlier ones finish, on whichever CU frees up first; it is
+ *                   enforced by reserving LDS per workgroup (the kernels use none).
  * Not every (M, R, U) combination is compiled; an unsupported one is GEMV_ERR_INVALID_ARG.
  */
 typedef struct {
@@ -72,6 +76,7 @@ typedef struct {
     int rows_per_wave;
     int waves_per_block;
     int unroll;
+    int waves_per_cu;
 } gemv_plan_opts;
 
 /*
@@ -100,6 +105,8 @@ typedef struct {
     int depth_bound;        /* h: the most fp32 roundings any product passes through */
     double bytes_in_flight_per_cu;   /* 16-byte W loads outstanding per CU at full residency */
     double bytes_in_flight_needed;   /* Little's law per CU: bandwidth * latency / CUs     */
+    int waves_per_cu;       /* resident-wave cap per CU, 0 when the launch has none */
+    int lds_bytes;          /* LDS reserved per workgroup to enforce that cap (0: none) */
 } gemv_plan_info;
 
 /*
@@ -139,6 +146,7 @@ void gemv_plan_destroy(gemv_plan_t p);
  *   W   bf16 [n][ldw], ldw >= k, 2-byte aligned.
  *   X   bf16 [m][ldx], ldx >= k, 2-byte aligned (ldx is ignored when m == 1).
  *   Y   fp32 [m][ldy], ldy >= n, 4-byte aligned; overwritten.
+ *   Leading dimensions above 2^31 - 1 elements are GEMV_ERR_INVALID_ARG.
  *   workspace  device buffer of at least gemv_workspace_size(p) bytes, 4-byte aligned
  *              (NULL allowed when that size is 0). It holds the split partial sums and
  *              the tickets that pick, per row block, the workgroup that adds them up.

@@ -125,9 +125,59 @@ def test_bytes_in_flight_report():
     i = plan(4096, 14336).info
     assert i["bytes_in_flight_needed"] == pytest.approx(8e12 * 1e-6 / 256)
     waves = i["grid_x"] * i["grid_y"] * i["waves_per_block"]
-    per_cu = min(math.ceil(waves / 256), 32)
+    per_cu = min(math.ceil(waves / 256), 32, i["waves_per_cu"] or 32)
     assert i["bytes_in_flight_per_cu"] == per_cu * i["unroll"] * i["rows_per_wave"] * 1024
     assert i["bytes_in_flight_per_cu"] >= i["bytes_in_flight_needed"]
+
+
+# (n, k) -> (R, U, resident-wave cap) chosen from the measured MI355X sweeps
+BATCH1_TILES = {
+    (4096, 14336): (1, 4, 8),      # down_proj: 4096 one-row waves in two rounds of 8 per CU
+    (4097, 14337): (1, 4, 6),      # 17 waves per CU: three rounds of at most 6, not 8+8+1
+    (4096, 4096): (1, 4, 0),       # o_proj: 16 waves per CU, one uncapped round
+    (1024, 4096): (1, 4, 0),       # k_proj
+    (6144, 4096): (1, 8, 12),      # QKV: 24 waves per CU in two rounds of 12
+    (28672, 4096): (1, 8, 12),     # gate_up
+    (128256, 4096): (1, 8, 12),    # LM head: 501 waves per CU in 42 rounds of at most 12
+    (7, 129): (1, 2, 0),
+    (33, 1000): (1, 2, 0),
+}
+
+
+@pytest.mark.parametrize("nk", sorted(BATCH1_TILES))
+def test_batch1_tiles_and_caps(nk):
+    r, u, cap = BATCH1_TILES[nk]
+    i = plan(*nk).info
+    assert (i["rows_per_wave"], i["unroll"], i["waves_per_block"]) == (r, u, 1)
+    assert i["waves_per_cu"] == cap
+    if cap:
+        # at most `cap` single-wave workgroups share a CU's 160 KiB of LDS, and no more
+        assert cap * i["lds_bytes"] <= 160 * 1024 < (cap + 1) * i["lds_bytes"]
+        assert i["lds_bytes"] % 512 == 0
+        rounds = math.ceil(math.ceil(i["grid_x"] / 256) / cap)
+        assert math.ceil(i["grid_x"] / (256 * rounds)) == cap     # rounds equally full
+    else:
+        assert i["lds_bytes"] == 0
+
+
+def test_cap_only_for_unsplit_batch1():
+    assert plan(4096, 14336, 2).info["waves_per_cu"] == 0
+    assert plan(4096, 14336, splits=2).info["waves_per_cu"] == 0
+    assert plan(64, 14336).info["waves_per_cu"] == 0            # split plan
+
+
+def test_forced_cap():
+    i = plan(4096, 14336, waves_per_cu=5).info
+    assert i["waves_per_cu"] == 5 and 5 * i["lds_bytes"] <= 160 * 1024 < 6 * i["lds_bytes"]
+    assert plan(4096, 14336, waves_per_cu=-1).info["waves_per_cu"] == 0
+    # four waves per workgroup: the cap is a whole number of workgroups per CU
+    i = plan(4096, 14336, 2, waves_per_cu=10).info
+    assert i["waves_per_cu"] == 8 and i["waves_per_block"] == 4
+    for bad in (-2, 33):
+        with pytest.raises(bbd.GemvError):
+            plan(4096, 14336, waves_per_cu=bad)
+    with pytest.raises(bbd.GemvError):
+        plan(4096, 14336, 2, waves_per_cu=3)     # less than one four-wave workgroup
 
 
 @pytest.mark.timeout(120)
