@@ -355,106 +355,6 @@ __global__ void __launch_bounds__(512)
         combine_if_last<MULTI>(p, M, waves * R);
 }
 
-// ---------------------------------------------------------------------------- whole rows
-// The batch-1 decode shapes (K a multiple of 512 U, one row per wave, no split, one weight
-// matrix, 16-byte aligned) run a kernel with nothing else in it: a 32-byte argument block,
-// no slice arithmetic, no remainder paths, no output-routing branches. Measured on MI355X it
-// is 0.2-0.4 us per launch faster than the general kernel on the same tile (down_proj
-// 4096 x 14336: 18.3-18.4 us against 18.8 us). It sums every row in the same order as
-// gemv_fast, so the two give bitwise the same result.
-struct WholeArgs {
-    const uint16_t *w;      // row 0
-    const uint16_t *x;
-    float *y;
-    int32_t ldw;
-    int32_t bursts;         // K / (512 U)
-};
-
-template <int U>
-__global__ void __launch_bounds__(512)
-    __attribute__((amdgpu_waves_per_eu(1, fast_waves_per_simd<1, 1, U>()))) gemv_whole(WholeArgs a)
-{
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x;                       // one single-wave workgroup per row
-    const uint16_t *wp = a.w + (int64_t)row * a.ldw + kVecElems * lane;
-    const uint16_t *xp = a.x + kVecElems * lane;
-    float acc = 0.f;
-    for (int b = 0; b < a.bursts; ++b) {
-        u32x4 wv[U], xv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            wv[u] = load_stream(wp + kWaveStep * u);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            xv[u] = load_cached(xp + kWaveStep * u);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            acc = dot8(wv[u], xv[u], acc);
-        wp += kWaveStep * U;
-        xp += kWaveStep * U;
-    }
-    const float sum = lane63(wave_sum(acc));
-    if (lane == 0)
-        a.y[row] = sum;
-}
-
-// The fused form (QKV, gate_up): up to four weight matrices with one leading dimension,
-// each row's segment picked per wave from values held in scalar registers.
-struct WholeMultiArgs {
-    const uint16_t *w[GEMV_MAX_SEGMENTS];   // row 0 of each segment (segment 0 repeated)
-    float *y[GEMV_MAX_SEGMENTS];
-    const uint16_t *x;
-    int32_t ldw;
-    int32_t bursts;
-    int32_t row0[GEMV_MAX_SEGMENTS];        // first row of each segment; INT32_MAX unused
-};
-
-template <int U>
-__global__ void __launch_bounds__(512)
-    __attribute__((amdgpu_waves_per_eu(1, fast_waves_per_simd<1, 1, U>())))
-        gemv_whole_multi(WholeMultiArgs a)
-{
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x;
-    // Values, not member addresses, are selected (an address select would move the
-    // arguments to scratch); pointers are rebuilt as offsets from segment 0's.
-    uint64_t w[GEMV_MAX_SEGMENTS], y[GEMV_MAX_SEGMENTS];
-#pragma unroll
-    for (int i = 0; i < GEMV_MAX_SEGMENTS; ++i) {
-        w[i] = uniform64((uint64_t)a.w[i]);
-        y[i] = uniform64((uint64_t)a.y[i]);
-    }
-    const int j = (row >= a.row0[1]) + (row >= a.row0[2]) + (row >= a.row0[3]);
-    const uint64_t wj = j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : w[3];
-    const uint64_t yj = j == 0 ? y[0] : j == 1 ? y[1] : j == 2 ? y[2] : y[3];
-    const int local =
-        row - (j == 0 ? 0 : j == 1 ? a.row0[1] : j == 2 ? a.row0[2] : a.row0[3]);
-    const uint16_t *wp = a.w[0] + (int64_t)(wj - w[0]) / (int64_t)sizeof(uint16_t) +
-                         (int64_t)local * a.ldw + kVecElems * lane;
-    float *yp = a.y[0] + (int64_t)(yj - y[0]) / (int64_t)sizeof(float) + local;
-    const uint16_t *xp = a.x + kVecElems * lane;
-    float acc = 0.f;
-    for (int b = 0; b < a.bursts; ++b) {
-        u32x4 wv[U], xv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            wv[u] = load_stream(wp + kWaveStep * u);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            xv[u] = load_cached(xp + kWaveStep * u);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            acc = dot8(wv[u], xv[u], acc);
-        wp += kWaveStep * U;
-        xp += kWaveStep * U;
-    }
-    const float sum = lane63(wave_sum(acc));
-    if (lane == 0)
-        *yp = sum;
-}
-
 // ---------------------------------------------------------------------------- unaligned
 // Any 2-byte-aligned layout. Per row, the 16-byte vectors are placed where the row's W
 // address is 16-byte aligned (starting at element h, 0 <= h < 8); the up to 7 elements
@@ -593,19 +493,6 @@ const UnalignedTable kUnaligned[2][2] = {
     {unaligned_table<true, false>(std::make_index_sequence<GEMV_MAX_M>{}),
      unaligned_table<true, true>(std::make_index_sequence<GEMV_MAX_M>{})}};
 
-const void *find_whole(int u, bool multi)
-{
-    switch (u) {
-    case 2: return multi ? reinterpret_cast<const void *>(&gemv_whole_multi<2>)
-                         : reinterpret_cast<const void *>(&gemv_whole<2>);
-    case 4: return multi ? reinterpret_cast<const void *>(&gemv_whole_multi<4>)
-                         : reinterpret_cast<const void *>(&gemv_whole<4>);
-    case 8: return multi ? reinterpret_cast<const void *>(&gemv_whole_multi<8>)
-                         : reinterpret_cast<const void *>(&gemv_whole<8>);
-    default: return nullptr;
-    }
-}
-
 const void *find_fast(int m, int r, int u, bool split, bool multi)
 {
     for (size_t i = 0; i < kNumVariants; ++i)
@@ -665,46 +552,10 @@ gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void
     for (int i = 0; i < nseg; ++i)
         fast = fast && aligned16(segs[i].W) && segs[i].ldw % 8 == 0;
 
-    // Whole-row kernels: batch 1, one row per single-wave workgroup, no split, K a whole
-    // number of bursts, and (fused) one leading dimension for every segment.
-    bool same_ldw = true;
-    for (int i = 1; i < nseg; ++i)
-        same_ldw = same_ldw && segs[i].ldw == segs[0].ldw;
-    const void *whole = nullptr;
-    if (fast && same_ldw && p->m == 1 && p->rows_per_wave == 1 && p->waves_per_block == 1 &&
-        p->splits == 1 && p->k % ((int64_t)kWaveStep * p->unroll) == 0)
-        whole = find_whole(p->unroll, nseg > 1);
-    if (whole) {
-        WholeArgs wa;
-        WholeMultiArgs wm;
-        void *wargs[1];
-        const int32_t bursts = (int32_t)(p->k / ((int64_t)kWaveStep * p->unroll));
-        if (nseg == 1) {
-            wa.w = static_cast<const uint16_t *>(segs[0].W);
-            wa.x = static_cast<const uint16_t *>(X);
-            wa.y = segs[0].Y;
-            wa.ldw = (int32_t)segs[0].ldw;
-            wa.bursts = bursts;
-            wargs[0] = &wa;
-        } else {
-            int64_t row0 = 0;
-            for (int i = 0; i < GEMV_MAX_SEGMENTS; ++i) {
-                const int src = i < nseg ? i : 0;
-                wm.w[i] = static_cast<const uint16_t *>(segs[src].W);
-                wm.y[i] = segs[src].Y;
-                wm.row0[i] = i < nseg ? (int32_t)row0 : INT32_MAX;
-                if (i < nseg)
-                    row0 += segs[i].n;
-            }
-            wm.x = static_cast<const uint16_t *>(X);
-            wm.ldw = (int32_t)segs[0].ldw;
-            wm.bursts = bursts;
-            wargs[0] = &wm;
-        }
-        hipError_t e = hipLaunchKernel(whole, dim3((unsigned)p->grid_x), dim3(kWaveLanes), wargs,
-                                       (size_t)p->lds_bytes, static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? GEMV_OK : device_error(e);
-    }
+    bool done = false;
+    st = bbd::launch_whole(p, segs, nseg, X, stream, &done);
+    if (done || st != GEMV_OK)
+        return st;
 
     ArgsMulti a;
     memset(&a, 0, sizeof a);

@@ -58,6 +58,11 @@ constexpr Variant kVariants[] = {
 
 bool variant_supported(int m, int r, int u);
 
+// Launch a validated batch-1 call on the whole-row kernels (whole.hip) when it qualifies;
+// *done tells whether it did.
+gemv_status launch_whole(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
+                         void *stream, bool *done);
+
 // Record the HIP error code behind a GEMV_ERR_DEVICE / GEMV_ERR_CAPTURE for
 // gemv_last_hip_error() (thread-local) and return `status`.
 gemv_status record_hip_error(int hip_error, gemv_status status);
