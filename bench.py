@@ -31,7 +31,10 @@ PEAK_HBM = 8.0e12                 # MI355X HBM3E, published peak, B/s
 METRIC = "achieved HBM TB/s and % of peak, bf16 GEMV batch 1 at Llama-8B shapes"
 ROTATION_BYTES = 1.0e9            # >= 1 GB of distinct weights per rotation arena
 COUNTERS_FILE = os.path.join(HERE, "profiles", "counters_down_4096x14336.json")
-KERNEL_SOURCE = os.path.join(HERE, "bandwidth_bound_decode_amd", "csrc", "gemv.hip")
+# The headline (batch-1, whole-burst rows) kernel's sources; the committed counter summary
+# is valid only for the sources it was taken on.
+KERNEL_SOURCES = [os.path.join(HERE, "bandwidth_bound_decode_amd", "csrc", f)
+                  for f in ("whole.hip", "device.h")]
 
 # The pages' H100 SXM context (decode-GEMV page and GPU performance chains page).
 H100 = {"hbm_TBps": 3.35, "sms": 132, "k_proj_transfer_us_at_peak": 2.5,
@@ -66,8 +69,11 @@ def ridge(flops_per_s: float, bytes_per_s: float) -> float:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def counter_traffic(plan_info: dict):
