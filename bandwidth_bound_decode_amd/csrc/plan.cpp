@@ -62,14 +62,21 @@ void default_tile(int m, int64_t n, int64_t k, int cus, int *r, int *u, int *wav
             *u = 4;
         else
             *u = 8;
-    } else if (m <= 4) {
-        *r = 2;
+    } else if (m == 2) {
+        // 2 <= M <= 16: the tiles of the LDS-staged batch kernel (batch.hip), measured on
+        // MI355X at 4096 x 14336; each is also a compiled tile of the general kernel, which
+        // runs any call the batch kernel does not take.
+        *r = 1;
         *u = 4;
-        *waves = 4;
-    } else {
+        *waves = 8;
+    } else if (m <= 8) {
         *r = 2;
         *u = 2;
         *waves = 4;
+    } else {
+        *r = 2;
+        *u = 1;
+        *waves = 8;
     }
 }
 

@@ -54,6 +54,8 @@ constexpr Variant kVariants[] = {
     {9, 1, 2}, {9, 2, 2}, {10, 1, 2}, {10, 2, 2}, {11, 1, 2}, {11, 2, 2}, {12, 1, 2},
     {12, 2, 2}, {13, 1, 2}, {13, 2, 2}, {14, 1, 2}, {14, 2, 2}, {15, 1, 2}, {15, 2, 2},
     {16, 1, 2}, {16, 2, 2},
+    {9, 2, 1}, {10, 2, 1}, {11, 2, 1}, {12, 2, 1}, {13, 2, 1}, {14, 2, 1}, {15, 2, 1},
+    {16, 2, 1},
 };
 
 bool variant_supported(int m, int r, int u);
@@ -62,6 +64,11 @@ bool variant_supported(int m, int r, int u);
 // *done tells whether it did.
 gemv_status launch_whole(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
                          void *stream, bool *done);
+
+// Launch a validated 2 <= M <= 16 call on the LDS-staged batch kernel (batch.hip) when it
+// qualifies; *done tells whether it did.
+gemv_status launch_batch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
+                         int64_t ldx, void *stream, bool *done);
 
 // Record the HIP error code behind a GEMV_ERR_DEVICE / GEMV_ERR_CAPTURE for
 // gemv_last_hip_error() (thread-local) and return `status`.

@@ -64,7 +64,7 @@ typedef struct gemv_plan_s *gemv_plan_t;
  *   waves_per_block waves in a workgroup (1, 2, 4 or 8).
  *   unroll          U, independent 16-byte W loads per row each lane issues before using
  *                   any of them (cause 2 of the same section): 2, 4, 7, 8 or 14 (7 and 14
- *                   divide the 28 wave steps of a 14336-element row).
+ *                   divide the 28 wave steps of a 14336-element row); 1 for batches of 9-16.
  *   waves_per_cu    most waves of the launch resident on one CU at a time: 1..32, or -1
  *                   for no cap. A cap below what registers allow makes later workgroups
  *                   start as earlier ones finish, on whichever CU frees up first; it is

@@ -171,13 +171,21 @@ def test_forced_cap():
     assert i["waves_per_cu"] == 5 and 5 * i["lds_bytes"] <= 160 * 1024 < 6 * i["lds_bytes"]
     assert plan(4096, 14336, waves_per_cu=-1).info["waves_per_cu"] == 0
     # four waves per workgroup: the cap is a whole number of workgroups per CU
-    i = plan(4096, 14336, 2, waves_per_cu=10).info
+    i = plan(4096, 14336, 4, waves_per_cu=10).info
     assert i["waves_per_cu"] == 8 and i["waves_per_block"] == 4
     for bad in (-2, 33):
         with pytest.raises(bbd.GemvError):
             plan(4096, 14336, waves_per_cu=bad)
     with pytest.raises(bbd.GemvError):
-        plan(4096, 14336, 2, waves_per_cu=3)     # less than one four-wave workgroup
+        plan(4096, 14336, 4, waves_per_cu=3)     # less than one four-wave workgroup
+
+
+@pytest.mark.parametrize("m,tile", [(2, (1, 4, 8)), (3, (2, 2, 4)), (8, (2, 2, 4)),
+                                    (9, (2, 1, 8)), (16, (2, 1, 8))])
+def test_batch_tiles(m, tile):
+    i = plan(4096, 14336, m).info
+    assert (i["rows_per_wave"], i["unroll"], i["waves_per_block"]) == tile
+    assert i["splits"] == 1 and i["waves_per_cu"] == 0
 
 
 @pytest.mark.timeout(120)
