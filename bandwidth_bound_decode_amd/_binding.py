@@ -42,7 +42,7 @@ class GemvError(RuntimeError):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
                 ("waves_per_block", ctypes.c_int), ("unroll", ctypes.c_int),
-                ("waves_per_cu", ctypes.c_int)]
+                ("waves_per_cu", ctypes.c_int), ("mfma", ctypes.c_int)]
 
 
 class DeviceDesc(ctypes.Structure):
@@ -57,7 +57,9 @@ class PlanInfo(ctypes.Structure):
                 ("block_threads", ctypes.c_int), ("slice", ctypes.c_int64),
                 ("depth_bound", ctypes.c_int), ("bytes_in_flight_per_cu", ctypes.c_double),
                 ("bytes_in_flight_needed", ctypes.c_double), ("waves_per_cu", ctypes.c_int),
-                ("lds_bytes", ctypes.c_int)]
+                ("lds_bytes", ctypes.c_int), ("mfma", ctypes.c_int),
+                ("mfma_splits", ctypes.c_int), ("mfma_slice", ctypes.c_int64),
+                ("mfma_grid_x", ctypes.c_int), ("mfma_depth_bound", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -131,9 +133,9 @@ def bytes_in_flight(bytes_per_s: float, latency_s: float) -> float:
     return float(_lib.gemv_bytes_in_flight(bytes_per_s, latency_s))
 
 
-def _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu=0):
+def _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu=0, mfma=0):
     return PlanOpts(int(splits), int(rows_per_wave), int(waves_per_block), int(unroll),
-                    int(waves_per_cu))
+                    int(waves_per_cu), int(mfma))
 
 
 class Plan:
@@ -145,9 +147,9 @@ class Plan:
 
     def __init__(self, n: int, k: int, m: int = 1, device=None, *, splits: int = 0,
                  rows_per_wave: int = 0, waves_per_block: int = 0, unroll: int = 0,
-                 waves_per_cu: int = 0, desc: tuple | None = None):
+                 waves_per_cu: int = 0, mfma: int = 0, desc: tuple | None = None):
         self._h = ctypes.c_void_p()
-        opts = _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu)
+        opts = _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu, mfma)
         if desc is not None:
             d = DeviceDesc(int(desc[0]), float(desc[1]), float(desc[2]))
             st = _lib.gemv_plan_for(ctypes.byref(self._h), n, k, m, ctypes.byref(d),

@@ -556,6 +556,9 @@ gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void
     st = bbd::launch_whole(p, segs, nseg, X, stream, &done);
     if (done || st != GEMV_OK)
         return st;
+    st = bbd::launch_mfma(p, segs, nseg, X, ldx, ws, stream, &done);
+    if (done || st != GEMV_OK)
+        return st;
     st = bbd::launch_batch(p, segs, nseg, X, ldx, stream, &done);
     if (done || st != GEMV_OK)
         return st;

@@ -135,6 +135,18 @@ int depth_for(int64_t slice, int s)
     return (int)(4 * per_lane + 1 + 2 + 6 + (s - 1));
 }
 
+// The same bound for the matrix-core kernel. The instruction's internal summation order is
+// not documented, so a product is charged 32 roundings inside the MFMA it enters (as if the
+// 32 products of a 16x16x32 step were added one at a time) and the running accumulator one
+// rounding per later MFMA of the wave's chain (two per 64-element chunk); then the 7 adds
+// of the other waves' partial tiles and S-1 combine additions.
+int mfma_depth_for(int64_t slice, int s)
+{
+    int64_t chunks = ceil_div(slice, kMfmaChunk);
+    int64_t turns = ceil_div(chunks, kMfmaWaves);
+    return (int)(32 + (kMfmaChunk / 32) * turns + (kMfmaWaves - 1) + (s - 1));
+}
+
 bool valid_waves(int w) { return w == 1 || w == 2 || w == 4 || w == 8; }
 
 }  // namespace
@@ -157,11 +169,11 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     // Row indices and grid sizes are held in 32 bits on the device.
     if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30)
         return GEMV_ERR_INVALID_ARG;
-    gemv_plan_opts o = {0, 0, 0, 0, 0};
+    gemv_plan_opts o = {0, 0, 0, 0, 0, 0};
     if (opts)
         o = *opts;
     if (o.splits < 0 || o.rows_per_wave < 0 || o.waves_per_block < 0 || o.unroll < 0 ||
-        o.waves_per_cu < -1 || o.waves_per_cu > kMaxWavesPerCU)
+        o.waves_per_cu < -1 || o.waves_per_cu > kMaxWavesPerCU || o.mfma < -1 || o.mfma > 1)
         return GEMV_ERR_INVALID_ARG;
 
     int r, u, waves;
@@ -240,6 +252,33 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
         }
     }
 
+    // Matrix-core launch for batches: 32-row workgroups, split over K (with the same
+    // deterministic combine) only while the row blocks alone leave CUs without one.
+    int mf = 0, mf_s = 1, mf_depth = 0;
+    int64_t mf_slice = k;
+    const int64_t mf_grid = ceil_div(n, kMfmaRowsPerBlock);
+    {
+        const bool forced = o.splits || o.rows_per_wave || o.waves_per_block || o.unroll ||
+                            o.waves_per_cu;
+        const bool want_mf = o.mfma > 0 ? m >= 2 : o.mfma == 0 && m >= kMfmaMinBatch && !forced;
+        if (want_mf && k % kMfmaChunk == 0) {
+            int64_t want = mf_grid >= dev->compute_units ? 1 : ceil_div(dev->compute_units, mf_grid);
+            int64_t cap = k / kMfmaChunk / kMfmaWaves;   // every wave keeps a chunk per slice
+            if (want > cap)
+                want = cap > 1 ? cap : 1;
+            if (want > kMaxSplits)
+                want = kMaxSplits;
+            for (int cand = (int)want; cand <= kMaxSplits; ++cand) {
+                mf_slice = round_up(ceil_div(k, cand), kMfmaChunk);
+                mf_s = (int)ceil_div(k, mf_slice);
+                mf_depth = mfma_depth_for(mf_slice, mf_s);
+                if (mf_depth <= kMaxDepth)
+                    break;
+            }
+            mf = mf_depth <= kMaxDepth;
+        }
+    }
+
     gemv_plan_s *p = new (std::nothrow) gemv_plan_s;
     if (!p)
         return GEMV_ERR_INVALID_ARG;
@@ -258,12 +297,21 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     p->grid_y = s;
     p->block_threads = kWaveLanes * waves;
     p->depth_bound = depth_for(slice, s);
-    if (s > 1) {
+    p->mfma = mf;
+    p->mfma_splits = mf ? mf_s : 0;
+    p->mfma_slice = mf ? mf_slice : 0;
+    p->mfma_grid_x = mf ? (int)mf_grid : 0;
+    p->mfma_depth = mf ? mf_depth : 0;
+    const int ws_splits = mf && mf_s > s ? mf_s : s;
+    if (ws_splits > 1) {
         // One arrival ticket per row block (in a fixed-size region), then S x M x N fp32
-        // partial sums.
+        // partial sums, for whichever launch splits more.
         int64_t slots = p->grid_x > kTicketSlots ? p->grid_x : kTicketSlots;
+        if (mf && mf_grid > slots)
+            slots = mf_grid;
         p->partial_offset = (size_t)round_up(slots * (int64_t)sizeof(unsigned), 256);
-        p->workspace = p->partial_offset + (size_t)s * (size_t)m * (size_t)n * sizeof(float);
+        p->workspace =
+            p->partial_offset + (size_t)ws_splits * (size_t)m * (size_t)n * sizeof(float);
     }
 
     int64_t total_waves = (int64_t)p->grid_x * p->grid_y * waves;
@@ -299,6 +347,11 @@ extern "C" gemv_status gemv_plan_query(gemv_plan_t p, gemv_plan_info *info)
     info->bytes_in_flight_needed = p->bif_needed;
     info->waves_per_cu = p->waves_per_cu;
     info->lds_bytes = p->lds_bytes;
+    info->mfma = p->mfma;
+    info->mfma_splits = p->mfma_splits;
+    info->mfma_slice = p->mfma_slice;
+    info->mfma_grid_x = p->mfma_grid_x;
+    info->mfma_depth_bound = p->mfma_depth;
     return GEMV_OK;
 }
 

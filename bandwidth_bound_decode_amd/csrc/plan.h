@@ -36,6 +36,12 @@ constexpr int kOneRoundWavesPerCU = 16;   // short rows: up to this many waves p
 // many slots, so that plans with up to this many row blocks can share one workspace in any
 // order without one plan's partial sums landing on another plan's tickets.
 constexpr int64_t kTicketSlots = 4096;
+// Matrix-core kernel (mfma.hip): 32-row workgroups of 8 waves that take K in chunks of 64
+// elements; used by default from this batch size on (measured crossover at 4096 x 14336).
+constexpr int kMfmaRowsPerBlock = 32;
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaChunk = 64;
+constexpr int kMfmaMinBatch = 8;
 
 // One compiled (M, R, U) combination of the aligned fast-path kernel. The unaligned path
 // exists for every M and takes R at run time.
@@ -70,6 +76,11 @@ gemv_status launch_whole(gemv_plan_t p, const gemv_segment *segs, int nseg, cons
 gemv_status launch_batch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
                          int64_t ldx, void *stream, bool *done);
 
+// Launch a validated call on the matrix-core kernel (mfma.hip) when the plan chose it and
+// the call qualifies; *done tells whether it did.
+gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
+                        int64_t ldx, void *ws, void *stream, bool *done);
+
 // Record the HIP error code behind a GEMV_ERR_DEVICE / GEMV_ERR_CAPTURE for
 // gemv_last_hip_error() (thread-local) and return `status`.
 gemv_status record_hip_error(int hip_error, gemv_status status);
@@ -93,4 +104,9 @@ struct gemv_plan_s {
     double bif_per_cu, bif_needed;
     int waves_per_cu;           // resident-wave cap per CU (0: none)
     int lds_bytes;              // LDS reserved per workgroup to enforce the cap
+    int mfma;                   // aligned single-matrix calls run the matrix-core kernel
+    int mfma_splits;
+    int64_t mfma_slice;
+    int mfma_grid_x;
+    int mfma_depth;
 };

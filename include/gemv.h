@@ -69,6 +69,15 @@ typedef struct gemv_plan_s *gemv_plan_t;
  *                   for no cap. A cap below what registers allow makes later workgroups
  *                   start as earlier ones finish, on whichever CU frees up first; it is
  *                   enforced by reserving LDS per workgroup (the kernels use none).
+ *   mfma            the matrix-core kernel for batches (decode-GEMV page: past a handful of
+ *                   vectors the work stops being a matrix-vector product and matrix units
+ *                   start to pay): 0 = automatic (M >= 8 with no tile, split or cap
+ *                   forced), 1 = for any M >= 2, -1 = never. It needs K to be a multiple of
+ *                   64. It runs only for 16-byte-aligned single-matrix calls; other calls of
+ *                   the same plan take the VALU kernels the fields above describe. The
+ *                   VALU kernels sum every output in the same order at every M, so with
+ *                   -1 each row of a batched result is bitwise equal to its batch-1 result;
+ *                   the matrix-core kernel meets the same tolerance in another order.
  * Not every (M, R, U) combination is compiled; an unsupported one is GEMV_ERR_INVALID_ARG.
  */
 typedef struct {
@@ -77,6 +86,7 @@ typedef struct {
     int waves_per_block;
     int unroll;
     int waves_per_cu;
+    int mfma;
 } gemv_plan_opts;
 
 /*
@@ -107,6 +117,13 @@ typedef struct {
     double bytes_in_flight_needed;   /* Little's law per CU: bandwidth * latency / CUs     */
     int waves_per_cu;       /* resident-wave cap per CU, 0 when the launch has none */
     int lds_bytes;          /* LDS reserved per workgroup to enforce that cap (0: none) */
+    /* The matrix-core launch, when mfma is 1 (aligned single-matrix calls run it; the
+       fields above then describe the kernels every other call of the plan takes). */
+    int mfma;
+    int mfma_splits;        /* K slices; > 1 uses the workspace like a VALU split */
+    int64_t mfma_slice;     /* K elements per slice, a multiple of 64 */
+    int mfma_grid_x;        /* 32-row blocks: ceil(N / 32); 8 waves per workgroup */
+    int mfma_depth_bound;   /* h for that kernel, counting 32 roundings per MFMA */
 } gemv_plan_info;
 
 /*
@@ -132,7 +149,8 @@ gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int m,
 /*
  * Bytes of workspace gemv_run needs: 0 when S == 1; otherwise a ticket region of
  * 4 * max(grid_x, 4096) bytes (one 32-bit arrival counter per row block) followed by the
- * S*M*N fp32 partial sums. 0 for a NULL plan.
+ * S*M*N fp32 partial sums. A plan with both a split VALU launch and a split matrix-core
+ * launch needs the larger of the two. 0 for a NULL plan.
  */
 size_t gemv_workspace_size(gemv_plan_t p);
 

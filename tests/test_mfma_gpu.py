@@ -1,0 +1,107 @@
+"""GPU parity of the matrix-core batch kernel: within tolerance of the oracle at the
+down_proj shape and on small shapes that span several 32-row blocks with a ragged last one,
+unsplit and split over K; exact where every partial sum is exact (identity, one-hot, constant
+W); reproducible bit for bit; and the unaligned fallback equal to the VALU plan."""
+import numpy as np
+import pytest
+import torch
+
+import bandwidth_bound_decode_amd as bbd
+from gpu_helpers import bits_equal, device_matrix, draw, gemv, oracle_check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("m", [8, 12])
+def test_down_proj_batches(m):
+    w, x = draw(4096, 14336, m, seed=300 + m)
+    W, X = device_matrix(w), device_matrix(x)
+    Y, p = gemv(W, X)
+    assert p.info["mfma"] == 1 and p.info["mfma_splits"] == 2, p.info
+    oracle_check(W, X, Y, f"mfma down m={m}")
+    Y2, _ = gemv(W, X, plan=p)
+    assert bits_equal(Y, Y2), "not reproducible"
+
+
+@pytest.mark.parametrize("n,k", [(300, 5120), (33, 4096), (8200, 1024), (1, 64), (47, 192)])
+def test_shapes_every_batch(n, k):
+    """Ragged row blocks, one slice and split slices (the combine), every M from 2."""
+    for m in range(2, 17):
+        w, x = draw(n, k, m, seed=n + k + m)
+        W, X = device_matrix(w), device_matrix(x)
+        p = bbd.Plan(n, k, m, mfma=1)
+        assert p.info["mfma"] == 1
+        Y, _ = gemv(W, X, plan=p)
+        oracle_check(W, X, Y, f"mfma n={n} k={k} m={m} S={p.info['mfma_splits']}")
+        Y2, _ = gemv(W, X, plan=p)         # the tickets were left at zero for this call
+        assert bits_equal(Y, Y2), f"n={n} k={k} m={m} not reproducible"
+
+
+def test_identity_and_one_hot_exact():
+    n = k = 512
+    _, x = draw(1, k, 16, seed=7)
+    eye = torch.eye(n, dtype=torch.bfloat16)
+    Y, p = gemv(device_matrix(eye), device_matrix(x), mfma=1)
+    assert p.info["mfma"] == 1
+    assert bits_equal(Y, x.float()), "W = I must return X exactly"
+    w, _ = draw(300, 4096, 1, seed=8)
+    cols = [0, 1, 31, 32, 63, 64, 511, 512, 2047, 2048, 4032, 4095, 7, 100, 3000, 4094]
+    xo = torch.zeros(16, 4096, dtype=torch.bfloat16)
+    for i, c in enumerate(cols):
+        xo[i, c] = 1.0
+    Y, p = gemv(device_matrix(w), device_matrix(xo), mfma=1)
+    assert p.info["mfma_splits"] > 1
+    for i, c in enumerate(cols):
+        assert bits_equal(Y[i], w[:, c].float()), f"one-hot column {c}"
+
+
+def test_constant_w_exact():
+    """W = 2^-6 and x in {-2..2}: every partial sum is an exact fp32 value in any order."""
+    n, k, m = 300, 5120, 16
+    w = torch.full((n, k), 2.0 ** -6, dtype=torch.bfloat16)
+    rng = np.random.default_rng(n + k)
+    xi = rng.integers(-2, 3, size=(m, k))
+    x = torch.from_numpy(xi.astype(np.float32)).to(torch.bfloat16)
+    Y, _ = gemv(device_matrix(w), device_matrix(x), mfma=1)
+    want = torch.from_numpy((2.0 ** -6 * xi.sum(axis=1)).astype(np.float32))
+    assert bits_equal(Y, want[:, None].expand(m, n))
+
+
+def test_accumulator_rounded_once_per_mfma():
+    """Pin of the depth model: the running accumulator enters an MFMA's sum once, not ahead
+    of each product. K = 64 is one chunk (two MFMAs in order on one wave): the first gives
+    exactly 1.0, the second adds 32 products of 2^-25. Summed exactly that is 1 + 2^-20; an
+    accumulator rounded after every product would stay at 1.0."""
+    n, k, m = 16, 64, 16
+    w = torch.zeros(n, k, dtype=torch.bfloat16)
+    w[:, 0] = 1.0
+    w[:, 32:] = 2.0 ** -25
+    x = torch.ones(m, k, dtype=torch.bfloat16)
+    Y, p = gemv(device_matrix(w), device_matrix(x), mfma=1)
+    assert p.info["mfma"] == 1 and p.info["mfma_splits"] == 1
+    assert bits_equal(Y, torch.full((m, n), 1.0 + 2.0 ** -20)), Y[0, :4].tolist()
+
+
+def test_special_values():
+    n, k, m = 64, 1024, 9
+    w, x = draw(n, k, m, seed=10)
+    w[3, 17] = float("inf")
+    w[5, 900] = float("nan")
+    x[:, 17] = 1.0
+    Y, _ = gemv(device_matrix(w), device_matrix(x), mfma=1)
+    assert torch.isinf(Y[:, 3]).all() and torch.isnan(Y[:, 5]).all()
+    keep = [i for i in range(n) if i not in (3, 5)]
+    assert torch.isfinite(Y[:, keep]).all()
+
+
+def test_unaligned_call_takes_the_valu_kernels():
+    n, k, m = 100, 2048, 16
+    w, x = draw(n, k, m, seed=11)
+    W = device_matrix(w, ld=2056, offset=1)          # rows not 16-byte aligned
+    X = device_matrix(x)
+    p = bbd.Plan(n, k, m)
+    assert p.info["mfma"] == 1
+    Y, _ = gemv(W, X, plan=p)
+    oracle_check(W, X, Y, "unaligned fallback")
+    Yv, _ = gemv(W, X, mfma=-1)
+    assert bits_equal(Y, Yv), "fallback differs from the VALU plan"

@@ -69,12 +69,21 @@ def test_mi355x_plans(n, k, m):
     if info["slice"] > 512:
         assert info["slice"] % 512 == 0
     assert (s - 1) * info["slice"] < k <= s * info["slice"]
-    if s > 1:
-        tickets = 4 * max(info["grid_x"], 4096)
-        assert p.workspace_size == tickets + s * m * n * 4
+    ws_splits = max(s, info["mfma_splits"] if info["mfma"] else 1)
+    if ws_splits > 1:
+        tickets = 4 * max(info["grid_x"], info["mfma_grid_x"], 4096)
+        assert p.workspace_size == tickets + ws_splits * m * n * 4
         assert info["grid_x"] <= 4096         # automatic split plans can share a workspace
     else:
         assert p.workspace_size == 0
+    if info["mfma"]:
+        ms, msl = info["mfma_splits"], info["mfma_slice"]
+        assert m >= 8 and k % 64 == 0 and msl % 64 == 0
+        assert (ms - 1) * msl < k <= ms * msl
+        assert info["mfma_grid_x"] == math.ceil(n / 32)
+        assert info["mfma_depth_bound"] <= 160
+        # one 8-wave workgroup per CU at least, or no split because the rows cover them
+        assert info["mfma_grid_x"] * ms >= 256 or ms == k // 512
     # the tolerance 1e-5 * sum|terms| is guaranteed: gamma_h < 1e-5 for h <= 160
     assert info["depth_bound"] <= 160
     h = info["depth_bound"]
@@ -205,3 +214,33 @@ def test_plan_search_terminates_for_any_shape():
                 assert k > 700000, (n, k)
                 continue
             assert info["depth_bound"] <= 160 and info["splits"] >= 1, (n, k)
+
+
+def test_mfma_plans():
+    """The matrix-core launch: chosen from M = 8 with no tile option forced, split over K
+    only while 32-row blocks leave CUs without one, and its partials fit the workspace."""
+    i = plan(4096, 14336, 16).info
+    assert (i["mfma"], i["mfma_splits"], i["mfma_grid_x"], i["mfma_slice"]) == (1, 2, 128, 7168)
+    # 32 roundings in the first MFMA, 2 per later chunk of the wave's 14, 7 wave adds, 1 combine
+    assert i["mfma_depth_bound"] == 32 + 2 * 14 + 7 + 1
+    assert plan(4096, 14336, 16).workspace_size == 4 * 4096 + 2 * 16 * 4096 * 4
+    assert plan(4096, 14336, 8).info["mfma"] == 1
+    assert plan(4096, 14336, 7).info["mfma"] == 0
+    assert plan(4096, 14336, 16, mfma=-1).info["mfma"] == 0
+    assert plan(4096, 14336, 16, mfma=-1).workspace_size == 0
+    assert plan(4096, 14336, 2, mfma=1).info["mfma"] == 1
+    assert plan(4096, 14336, 1, mfma=1).info["mfma"] == 0
+    assert plan(4097, 14337, 16).info["mfma"] == 0          # K not a multiple of 64
+    assert plan(33, 1000, 16).info["mfma"] == 0
+    assert plan(4096, 14336, 16, splits=2).info["mfma"] == 0     # forced VALU options
+    assert plan(4096, 14336, 16, unroll=2).info["mfma"] == 0
+    assert plan(4096, 14336, 16, splits=2, mfma=1).info["mfma"] == 1
+    g = plan(28672, 4096, 16).info                            # 896 blocks: no split
+    assert (g["mfma"], g["mfma_splits"]) == (1, 1)
+    assert plan(28672, 4096, 16).workspace_size == 0
+    small = plan(33, 4096, 9).info                            # 2 blocks: split to the cap
+    assert small["mfma_splits"] == 4096 // 512 and small["mfma_slice"] == 512
+    long_k = plan(64, 1 << 19, 16).info                       # accuracy forces the split
+    assert long_k["mfma"] == 1 and long_k["mfma_depth_bound"] <= 160
+    with pytest.raises(bbd.GemvError):
+        plan(4096, 14336, 16, mfma=2)
