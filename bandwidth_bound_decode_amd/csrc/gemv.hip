@@ -267,7 +267,7 @@ __device__ __forceinline__ void fast_rows(const ArgsT<MULTI> &p, int row_first, 
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int m = 0; m < M; ++m)
-                xv[u][m] = load_cached(xk + m * p.ldx + 8 * (lane + 64 * (step + u)));
+                xv[u][m] = load_cached(xk + (int64_t)m * p.ldx + 8 * (lane + 64 * (step + u)));
         // Keep the whole burst of loads ahead of the first use: without this the
         // scheduler interleaves waits into it to save registers, cutting loads in flight.
         __builtin_amdgcn_sched_barrier(0);
@@ -296,7 +296,7 @@ __device__ __forceinline__ void fast_rows(const ArgsT<MULTI> &p, int row_first, 
             if (u < rest)
 #pragma unroll
                 for (int m = 0; m < M; ++m)
-                    xv[u][m] = load_cached(xk + m * p.ldx + 8 * (lane + 64 * (step + u)));
+                    xv[u][m] = load_cached(xk + (int64_t)m * p.ldx + 8 * (lane + 64 * (step + u)));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -316,7 +316,7 @@ __device__ __forceinline__ void fast_rows(const ArgsT<MULTI> &p, int row_first, 
             wv[r] = load_stream(wrow[r] + 8 * v_last);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            u32x4 xv = load_cached(xk + m * p.ldx + 8 * v_last);
+            u32x4 xv = load_cached(xk + (int64_t)m * p.ldx + 8 * v_last);
 #pragma unroll
             for (int r = 0; r < R; ++r)
                 acc[r][m] = dot8(wv[r], xv, acc[r][m]);
@@ -330,7 +330,7 @@ __device__ __forceinline__ void fast_rows(const ArgsT<MULTI> &p, int row_first, 
             float w = bf16_to_f32(wrow[r][kk]);
 #pragma unroll
             for (int m = 0; m < M; ++m)
-                acc[r][m] = fmaf(w, bf16_to_f32(xk[m * p.ldx + kk]), acc[r][m]);
+                acc[r][m] = fmaf(w, bf16_to_f32(xk[(int64_t)m * p.ldx + kk]), acc[r][m]);
         }
     }
     finish<M, R, MULTI>(p, acc, row_first, split, lane);
@@ -359,27 +359,27 @@ __global__ void __launch_bounds__(512)
 // Any 2-byte-aligned layout. Per row, the 16-byte vectors are placed where the row's W
 // address is 16-byte aligned (starting at element h, 0 <= h < 8); the up to 7 elements
 // before the first vector and after the last one are scalar. The matching x window sits
-// at a shift q (per row and batch) from X's own 16-byte grid; it is built from the two
-// aligned x vectors around it, or element by element near the ends of a row of X.
+// at a shift q (per row and batch) from X's own 16-byte grid; it is read as five dwords
+// from the 4-byte boundary at or just below it and shifted into place, or element by
+// element near the ends of a row of X.
 
-// Elements q .. q+7 of the 16-element concatenation a|b (wave-uniform q in 0..7).
-__device__ __forceinline__ u32x4 funnel(u32x4 a, u32x4 b, int q)
+typedef unsigned int u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// x[k .. k+7] for k >= 1 and k + 10 <= K, q as below: the window starts at an element
+// offset of q & 1 from a 4-byte boundary, so four dwords from there and one more hold it,
+// and a byte shift of 0 or 2 per dword extracts it (no data-dependent select).
+__device__ __forceinline__ u32x4 x_window_interior(const uint16_t *xr, int k, int q)
 {
-    unsigned d0 = a.x, d1 = a.y, d2 = a.z, d3 = a.w;
-    unsigned d4 = b.x, d5 = b.y, d6 = b.z, d7 = b.w;
-    unsigned s0, s1, s2, s3, s4;
-    switch (q >> 1) {
-    case 0: s0 = d0; s1 = d1; s2 = d2; s3 = d3; s4 = d4; break;
-    case 1: s0 = d1; s1 = d2; s2 = d3; s3 = d4; s4 = d5; break;
-    case 2: s0 = d2; s1 = d3; s2 = d4; s3 = d5; s4 = d6; break;
-    default: s0 = d3; s1 = d4; s2 = d5; s3 = d6; s4 = d7; break;
-    }
+    const unsigned *d = reinterpret_cast<const unsigned *>(xr + k - (q & 1));
+    const u32x4 a = *reinterpret_cast<const u32x4_a4 *>(d);
+    const unsigned e = d[4];
     const unsigned sh = (unsigned)(q & 1) * 2u;   // bytes
+    const unsigned a0 = a.x, a1 = a.y, a2 = a.z, a3 = a.w;
     u32x4 r;
-    r.x = __builtin_amdgcn_alignbyte(s1, s0, sh);
-    r.y = __builtin_amdgcn_alignbyte(s2, s1, sh);
-    r.z = __builtin_amdgcn_alignbyte(s3, s2, sh);
-    r.w = __builtin_amdgcn_alignbyte(s4, s3, sh);
+    r.x = __builtin_amdgcn_alignbyte(a1, a0, sh);
+    r.y = __builtin_amdgcn_alignbyte(a2, a1, sh);
+    r.z = __builtin_amdgcn_alignbyte(a3, a2, sh);
+    r.w = __builtin_amdgcn_alignbyte(e, a3, sh);
     return r;
 }
 
@@ -387,10 +387,8 @@ __device__ __forceinline__ u32x4 funnel(u32x4 a, u32x4 b, int q)
 // 16-byte grid.
 __device__ __forceinline__ u32x4 x_window(const uint16_t *xr, int k, int K, int q)
 {
-    if (k >= 8 && k + 16 <= K) {
-        const uint16_t *base = xr + (k - q);   // 16-byte aligned, inside the row
-        return funnel(load_cached(base), load_cached(base + 8), q);
-    }
+    if (k >= 1 && k + 10 <= K)
+        return x_window_interior(xr, k, q);
     u32x4 r;
     r.x = (unsigned)xr[k + 0] | ((unsigned)xr[k + 1] << 16);
     r.y = (unsigned)xr[k + 2] | ((unsigned)xr[k + 3] << 16);
@@ -399,9 +397,18 @@ __device__ __forceinline__ u32x4 x_window(const uint16_t *xr, int k, int K, int 
     return r;
 }
 
+// Vectors each lane loads before using any, per batch size: the x windows take two loads
+// per vector and batch row, so the burst shrinks as M grows (registers).
+template <int M>
+constexpr int unaligned_unroll()
+{
+    return M <= 3 ? 4 : M <= 6 ? 2 : 1;
+}
+
 template <int M, bool SPLIT, bool MULTI>
 __global__ void __launch_bounds__(512) gemv_unaligned(ArgsT<MULTI> p)
 {
+    constexpr int U = unaligned_unroll<M>();
     const int rows_per_wave = p.rows;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -425,19 +432,58 @@ __global__ void __launch_bounds__(512) gemv_unaligned(ArgsT<MULTI> p)
         int q[M];
 #pragma unroll
         for (int m = 0; m < M; ++m)
-            q[m] = (int)((((uintptr_t)(p.x + m * p.ldx) >> 1) + (unsigned)h) & 7u);
+            q[m] = (int)((((uintptr_t)(p.x + (int64_t)m * p.ldx) >> 1) + (unsigned)h) & 7u);
 
         float acc[1][M];
 #pragma unroll
         for (int m = 0; m < M; ++m)
             acc[0][m] = 0.f;
 
-        for (int v = lane; v < nvec; v += 64) {
-            const int kk = ka + 8 * v;
-            u32x4 wv = load_stream(wr + kk);
+        // Lane l takes vectors l, l + 64, ... in increasing order, in bursts of U per lane
+        // with every load of a burst issued before the first use. Vectors [vlo, vend) have
+        // their x windows inside every row of X with room for the five-dword read; a burst
+        // made only of those takes the short path, the others (the first when vector 0 sits
+        // at the very start of X, and the last, partial one) clamp their loads and window
+        // reads into range and drop the out-of-range vectors from the sums.
+        const int vlo = ka >= 1 ? 0 : 1;
+        const int vhi = p.k - 10 - ka >= 0 ? ((p.k - 10 - ka) >> 3) + 1 : 0;
+        const int vend = max(vlo, min(nvec, vhi));
+        for (int v0 = 0; v0 < nvec; v0 += 64 * U) {
+            u32x4 wv[U], xv[U][M];
+            if (v0 >= vlo && v0 + 64 * U <= vend) {
 #pragma unroll
-            for (int m = 0; m < M; ++m)
-                acc[0][m] = dot8(wv, x_window(p.x + m * p.ldx, kk, p.k, q[m]), acc[0][m]);
+                for (int u = 0; u < U; ++u)
+                    wv[u] = load_stream(wr + ka + 8 * (v0 + lane + 64 * u));
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        xv[u][m] = x_window_interior(p.x + (int64_t)m * p.ldx,
+                                                     ka + 8 * (v0 + lane + 64 * u), q[m]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        acc[0][m] = dot8(wv[u], xv[u][m], acc[0][m]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    wv[u] = load_stream(wr + ka + 8 * min(v0 + lane + 64 * u, nvec - 1));
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        xv[u][m] = x_window(p.x + (int64_t)m * p.ldx,
+                                            ka + 8 * min(v0 + lane + 64 * u, nvec - 1), p.k, q[m]);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const bool in = v0 + lane + 64 * u < nvec;
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        acc[0][m] = in ? dot8(wv[u], xv[u][m], acc[0][m]) : acc[0][m];
+                }
+            }
         }
         // Lanes 0..7 take the head elements, lanes 8..15 the tail elements.
         const int kk = lane < 8 ? k0 + lane : tail_begin + (lane - 8);
@@ -446,7 +492,7 @@ __global__ void __launch_bounds__(512) gemv_unaligned(ArgsT<MULTI> p)
             float w = bf16_to_f32(wr[kk]);
 #pragma unroll
             for (int m = 0; m < M; ++m)
-                acc[0][m] = fmaf(w, bf16_to_f32(p.x[m * p.ldx + kk]), acc[0][m]);
+                acc[0][m] = fmaf(w, bf16_to_f32(p.x[(int64_t)m * p.ldx + kk]), acc[0][m]);
         }
         finish<M, 1, MULTI>(p, acc, row, split, lane);
     }
