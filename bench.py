@@ -364,8 +364,13 @@ def main(argv=None):
         for name, gg, ww, xx, segs in shapes:
             r, _, _, _ = bench_gemv(torch, bbd, gg, ww, xx, args.shape_steps, 10, segs)
             r["name"] = name
-            r["plan"] = {k: r["plan"][k] for k in ("splits", "rows_per_wave", "unroll",
-                                                   "grid_x", "grid_y")}
+            info = r["plan"]
+            r["plan"] = {k: info[k] for k in ("splits", "rows_per_wave", "unroll",
+                                              "grid_x", "grid_y")}
+            if info["mfma"]:      # aligned calls of this plan run the matrix-core kernel
+                r["plan"] = {"kernel": "gemv_mfma", "splits": info["mfma_splits"],
+                             "rows_per_block": 32, "grid_x": info["mfma_grid_x"],
+                             "grid_y": info["mfma_splits"]}
             for k in list(r):
                 if isinstance(r[k], float):
                     r[k] = round(r[k], 3)

@@ -266,3 +266,16 @@ def test_maximum_batch_and_long_k():
     Y, p = gemv(W, X)
     assert p.info["splits"] >= 2
     oracle_check(W, X, Y, "K=2^19")
+
+
+def test_large_x_stride():
+    """Batch rows of X more than 2^31 / 16 elements apart: m * ldx must not wrap in 32 bits
+    (aligned, unaligned and matrix-core paths)."""
+    for k, ldx, m in ((1000, 150_000_000, 16), (1000, 150_000_001, 3), (1024, 150_000_000, 16)):
+        w, x = draw(64, k, m, seed=k + m)
+        W = device_matrix(w)
+        X = device_matrix(x, ld=ldx)
+        Y, p = gemv(W, X)
+        oracle_check(W, X, Y, f"k={k} ldx={ldx} m={m} mfma={p.info['mfma']}")
+        del X
+        torch.cuda.empty_cache()
