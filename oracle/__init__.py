@@ -47,6 +47,12 @@ def _bind(so):
     so.oracle_bf16_to_f64.restype = None
     so.oracle_gemv_f64.argtypes = [p, i64, i64, i64, p, i64, i64, p, p, ctypes.c_int]
     so.oracle_gemv_f64.restype = ctypes.c_int
+    if hasattr(so, "oracle_gemv_q4_f64"):
+        so.oracle_q4_dequant_f64.argtypes = [p, i64, i64, i64, p, i64, p]
+        so.oracle_q4_dequant_f64.restype = ctypes.c_int
+        so.oracle_gemv_q4_f64.argtypes = [p, i64, i64, i64, p, i64, p, i64, i64, p, p,
+                                          ctypes.c_int]
+        so.oracle_gemv_q4_f64.restype = ctypes.c_int
     return so
 
 
@@ -95,6 +101,61 @@ def gemv(w_bits, x_bits, nthreads: int = 0, so=None):
                             y.ctypes.data, s.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError("oracle_gemv_f64 rejected its arguments")
+    return y, s
+
+
+Q4_GROUP = 128
+
+
+def _q4_args(wq, scales, k):
+    wq = np.asarray(wq)
+    sc = _u16(scales)
+    if wq.dtype != np.uint8 or wq.ndim != 2 or sc.ndim != 2:
+        raise TypeError("packed INT4 weights must be uint8 [n, >=ceil(k/2)], scales uint16 2-D")
+    if wq.shape[1] < (k + 1) // 2 or sc.shape[1] < (k + Q4_GROUP - 1) // Q4_GROUP:
+        raise ValueError("packed rows or scale rows too short for k")
+    if sc.shape[0] != wq.shape[0]:
+        raise ValueError("one scale row per weight row")
+    for a, item in ((wq, 1), (sc, 2)):
+        if a.shape[1] > 1 and a.strides[1] != item:
+            raise ValueError("rows must be contiguous")
+    n = wq.shape[0]
+    ldq = wq.strides[0] if n > 1 else wq.shape[1]
+    lds = sc.strides[0] // 2 if n > 1 else sc.shape[1]
+    return wq, sc, n, ldq, lds
+
+
+def q4_dequant(wq, scales, k: int, so=None) -> np.ndarray:
+    """fp64 [n, k] values of packed INT4 weights (the format in gemv_oracle.c)."""
+    so = so or lib()
+    wq, sc, n, ldq, lds = _q4_args(wq, scales, k)
+    out = np.empty((n, k), dtype=np.float64)
+    if n and k and so.oracle_q4_dequant_f64(wq.ctypes.data, n, k, ldq, sc.ctypes.data, lds,
+                                            out.ctypes.data) != 0:
+        raise ValueError("oracle_q4_dequant_f64 rejected its arguments")
+    return out
+
+
+def gemv_q4(wq, scales, x_bits, nthreads: int = 0, so=None):
+    """y_ref, s_abs for packed INT4 W (uint8 [n, >= ceil(k/2)] bytes, bf16 scale bits
+    [n, >= ceil(k/128)]) and bf16 X [m, k] (or [k]); float64 arrays [m, n]."""
+    so = so or lib()
+    x = _u16(x_bits)
+    if x.ndim == 1:
+        x = x[None, :]
+    m, k = x.shape
+    wq, sc, n, ldq, lds = _q4_args(wq, scales, k)
+    if n == 0 or m == 0 or k == 0:
+        return np.zeros((m, n)), np.zeros((m, n))
+    if x.shape[1] > 1 and x.strides[1] != 2:
+        raise ValueError("rows must be contiguous")
+    ldx = x.strides[0] // 2 if m > 1 else max(k, 1)
+    y = np.empty((m, n), dtype=np.float64)
+    s = np.empty((m, n), dtype=np.float64)
+    rc = so.oracle_gemv_q4_f64(wq.ctypes.data, n, k, ldq, sc.ctypes.data, lds, x.ctypes.data,
+                               m, ldx, y.ctypes.data, s.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gemv_q4_f64 rejected its arguments")
     return y, s
 
 

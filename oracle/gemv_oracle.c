@@ -97,3 +97,70 @@ int oracle_gemv_f64(const uint16_t *W, int64_t N, int64_t K, int64_t ldw,
     }
     return 0;
 }
+
+/*
+ * INT4 weights. The decode-GEMV page's follow-up turns the weights into INT4: a quarter of
+ * the bytes, unpacked in registers while the next loads are in flight. It fixes no storage
+ * format; the one this oracle defines (and the GPU path reads):
+ *   - a weight is a signed 4-bit integer v in [-8, 7], stored as a two's-complement nibble;
+ *   - row n of the packed matrix starts at Wq + n*ldq (bytes); element k is the low nibble
+ *     of byte k/2 when k is even and the high nibble when k is odd (so the 32-bit word
+ *     holding elements 8j..8j+7 has element 8j+i in bits 4i..4i+3);
+ *   - each run of 128 consecutive elements of a row (group k/128) shares one bf16 scale,
+ *     scale[n][g] at Sc + n*lds + g;
+ *   - the weight's value is v * scale.
+ * v has 4 significant bits and the scale 8, so the weight and its product with a bf16 x
+ * are exact in fp64; the only rounding is again the k-ascending fp64 summation.
+ */
+#define ORACLE_Q4_GROUP 128
+
+static double q4_weight(const uint8_t *row, const uint16_t *scales, int64_t j)
+{
+    int nibble = (j & 1) ? (row[j >> 1] >> 4) : (row[j >> 1] & 0x0F);
+    int v = nibble >= 8 ? nibble - 16 : nibble;
+    return (double)v * bf16_value(scales[j / ORACLE_Q4_GROUP]);
+}
+
+/* Dequantize an [N][K] INT4 matrix into fp64 out[n*K + j]. Returns 0, or -1. */
+int oracle_q4_dequant_f64(const uint8_t *Wq, int64_t N, int64_t K, int64_t ldq,
+                          const uint16_t *Sc, int64_t lds, double *out)
+{
+    if (!Wq || !Sc || !out || N < 0 || K < 0 || ldq < (K + 1) / 2 ||
+        lds < (K + ORACLE_Q4_GROUP - 1) / ORACLE_Q4_GROUP)
+        return -1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < K; ++j)
+            out[n * K + j] = q4_weight(Wq + n * ldq, Sc + n * lds, j);
+    return 0;
+}
+
+/*
+ * Y[m*N + n] = sum_j w_nj * X[m][j] with w from the INT4 format above, and
+ * Sabs[m*N + n] = sum_j |w_nj * X[m][j]|. X as for oracle_gemv_f64. Returns 0, or -1.
+ */
+int oracle_gemv_q4_f64(const uint8_t *Wq, int64_t N, int64_t K, int64_t ldq,
+                       const uint16_t *Sc, int64_t lds, const uint16_t *X, int64_t M,
+                       int64_t ldx, double *Y, double *Sabs, int nthreads)
+{
+    if (!Wq || !Sc || !X || !Y || !Sabs || N < 0 || K < 0 || M < 0 || ldq < (K + 1) / 2 ||
+        lds < (K + ORACLE_Q4_GROUP - 1) / ORACLE_Q4_GROUP || ldx < K)
+        return -1;
+    int threads = oracle_threads(nthreads);
+    (void)threads;
+#pragma omp parallel for schedule(static) num_threads(threads)
+    for (int64_t t = 0; t < M * N; ++t) {
+        const int64_t vec = t / N, row = t % N;
+        const uint8_t *packed = Wq + row * ldq;
+        const uint16_t *scales = Sc + row * lds;
+        const uint16_t *xv = X + vec * ldx;
+        double total = 0.0, magnitude = 0.0;
+        for (int64_t j = 0; j < K; j++) {
+            const double term = q4_weight(packed, scales, j) * bf16_value(xv[j]);
+            total += term;
+            magnitude += fabs(term);
+        }
+        Y[vec * N + row] = total;
+        Sabs[vec * N + row] = magnitude;
+    }
+    return 0;
+}

@@ -187,8 +187,90 @@ def pin_thread_invariance(so):
     assert np.array_equal(y1, y4) and np.array_equal(s1, s4), "thread count changes result"
 
 
+# --------------------------------------------------------------------------- INT4 weights
+def _bf16_bits(values) -> np.ndarray:
+    t = torch.tensor(np.asarray(values, dtype=np.float64)).to(torch.bfloat16)
+    back = t.to(torch.float64).numpy()
+    assert np.array_equal(back, np.asarray(values, dtype=np.float64)), "not exact in bf16"
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def pin_q4_format(so):
+    """Hand-decoded rows of the INT4 format: two's-complement nibbles, low nibble first,
+    one bf16 scale per 128 elements."""
+    # row 0: bytes 0x10 0x32 0x98 0xF7 -> nibbles 0,1,2,3,8,9,7,F -> 0,1,2,3,-8,-7,7,-1, x 0.5
+    # row 1: bytes 0x8F 0x7F 0x00 0x00 -> F,8,F,7,0,0,0,0 -> -1,-8,-1,7,0,0,0,0, x -2
+    wq = np.array([[0x10, 0x32, 0x98, 0xF7], [0x8F, 0x7F, 0x00, 0x00]], dtype=np.uint8)
+    sc = _bf16_bits([[0.5], [-2.0]])
+    want = np.array([[0, 0.5, 1, 1.5, -4, -3.5, 3.5, -0.5], [2, 16, 2, -14, 0, 0, 0, 0]])
+    got = oracle.q4_dequant(wq, sc, 8, so=so)
+    assert np.array_equal(got, want), f"format decode {got.tolist()}"
+    # groups: K = 260 elements all +1 (nibble pairs 0x11), scales 1, 2, 4 for elements
+    # 0..127, 128..255, 256..259; a padded row stride on both arrays
+    raw = np.full((1, 140), 0xEE, dtype=np.uint8)
+    raw[0, :130] = 0x11
+    sraw = _bf16_bits([[1.0, 2.0, 4.0, 1024.0]])
+    got = oracle.q4_dequant(raw, sraw, 260, so=so)[0]
+    want = np.concatenate([np.full(128, 1.0), np.full(128, 2.0), np.full(4, 4.0)])
+    assert np.array_equal(got, want), "group boundaries"
+    x = _bf16_bits(np.ones((1, 260)))
+    y, s = oracle.gemv_q4(raw, sraw, x, so=so)
+    assert y[0, 0] == 128 + 256 + 16 and s[0, 0] == y[0, 0], "group sums"
+
+
+def _q4_case(rng, n, k, ldq_pad=0, lds_pad=0):
+    """Random nibbles and power-of-two scales (so every weight is exact in bf16)."""
+    groups = (k + 127) // 128
+    wq = rng.integers(0, 256, size=(n, (k + 1) // 2 + ldq_pad), dtype=np.uint8)
+    scale = np.exp2(rng.integers(-12, 3, size=(n, groups + lds_pad)).astype(np.float64))
+    scale *= np.where(rng.random((n, groups + lds_pad)) < 0.3, -1.0, 1.0)
+    return wq, _bf16_bits(scale)
+
+
+def pin_q4_equals_bf16_oracle(so):
+    """With power-of-two scales every INT4 weight is a bf16 value, so the INT4 oracle must
+    equal the (separately pinned) bf16 oracle on those values bit for bit: same products,
+    same k-ascending sum. Odd K, a ragged last group, padded strides on every array."""
+    rng = np.random.default_rng(31)
+    for n, k, m in ((37, 300, 3), (5, 129, 1), (64, 1024, 2)):
+        wq, sc = _q4_case(rng, n, k, ldq_pad=3, lds_pad=2)
+        x = _rand_bits(rng, (m, k + 5), 1.0)[:, :k]
+        wdeq = oracle.q4_dequant(wq, sc, k, so=so)
+        y4, s4 = oracle.gemv_q4(wq, sc, x, so=so)
+        y, s = oracle.gemv(_bf16_bits(wdeq), x, so=so)
+        assert np.array_equal(y4, y) and np.array_equal(s4, s), f"q4 vs bf16 n={n} k={k}"
+
+
+def pin_q4_brute_force(so):
+    """Exact rational sums with weights decoded by hand from the nibbles, general scales."""
+    rng = np.random.default_rng(37)
+    n, k = 3, 200
+    wq = rng.integers(0, 256, size=(n, 100), dtype=np.uint8)
+    sc = _rand_bits(rng, (n, 2), 0.02)
+    x = _rand_bits(rng, (2, k), 1.0)
+    y, s = oracle.gemv_q4(wq, sc, x, so=so)
+    xs = [_exact(x[i]) for i in range(2)]
+    for r in range(n):
+        scales = _exact(sc[r])
+        w = []
+        for j in range(k):
+            b = int(wq[r, j // 2])
+            nib = (b >> 4) if j % 2 else (b & 0xF)
+            w.append((nib - 16 if nib >= 8 else nib) * scales[j // 128])
+        for i in range(2):
+            terms = [a * b for a, b in zip(w, xs[i])]
+            exact = sum(terms)
+            mag = sum(abs(t) for t in terms)
+            assert abs(Fraction(y[i, r]) - exact) <= Fraction(gamma(k)) * mag, "q4 brute force"
+            assert abs(Fraction(s[i, r]) - mag) <= Fraction(gamma(k)) * mag, "q4 s_abs"
+    zero = np.zeros((4, 100), dtype=np.uint8)
+    y, s = oracle.gemv_q4(zero, _bf16_bits(np.ones((4, 2))), x, so=so)
+    assert not y.any() and not s.any(), "all-zero weights"
+
+
 PINS = (pin_bf16_decode, pin_identity, pin_one_hot, pin_constant_w, pin_brute_force,
-        pin_cancellation, pin_numpy_matmul, pin_thread_invariance)
+        pin_cancellation, pin_numpy_matmul, pin_thread_invariance, pin_q4_format,
+        pin_q4_equals_bf16_oracle, pin_q4_brute_force)
 
 
 def run_all(lib_path: str) -> int:

@@ -74,6 +74,15 @@ MUTATIONS = {
     "w_index_transposed": ("bf16_value(w[k])", "bf16_value(W[k * ldw + n])"),
     "x_index_by_row": ("bf16_value(x[k])", "bf16_value(x[n % K])"),
     "stale_row_pointer": ("const uint16_t *w = W + n * ldw;", "const uint16_t *w = W + m * ldw;"),
+    "q4_unsigned_nibble": ("int v = nibble >= 8 ? nibble - 16 : nibble;", "int v = nibble;"),
+    "q4_nibble_order": ("(j & 1) ? (row[j >> 1] >> 4) : (row[j >> 1] & 0x0F)",
+                        "(j & 1) ? (row[j >> 1] & 0x0F) : (row[j >> 1] >> 4)"),
+    "q4_group_64": ("#define ORACLE_Q4_GROUP 128", "#define ORACLE_Q4_GROUP 64"),
+    "q4_scale_dropped": ("return (double)v * bf16_value(scales[j / ORACLE_Q4_GROUP]);",
+                         "return (double)v;"),
+    "q4_ignore_ldq": ("Wq + row * ldq", "Wq + row * ((K + 1) / 2)"),
+    "q4_ignore_lds": ("Sc + row * lds", "Sc + row * ((K + 127) / 128)"),
+    "q4_abs_without_fabs": ("magnitude += fabs(term);", "magnitude += term;"),
 }
 
 
