@@ -1,10 +1,10 @@
-"""MI355X-native decode GEMV: y = W.x with bf16 W and x, fp32 accumulation.
+"""MI355X-native decode GEMV: y = W.x with bf16 (or INT4) W, bf16 x, fp32 accumulation.
 
 The compute runs in hand-written gfx950 HIP kernels inside lib/libbbd_gemv.so (C ABI in
 include/gemv.h); this package is the thin ctypes binding over it.
 """
 from ._binding import (LIB_PATH, MAX_M, MAX_SEGMENTS, SIGNATURES, Chain, GemvError, Graph,
-                       Plan, Status, bytes_in_flight, fused_run, lib, run)
+                       Plan, Status, bytes_in_flight, fused_run, lib, run, run_int4)
 
 __all__ = ["LIB_PATH", "MAX_M", "MAX_SEGMENTS", "SIGNATURES", "Chain", "GemvError", "Graph",
-           "Plan", "Status", "bytes_in_flight", "fused_run", "lib", "run"]
+           "Plan", "Status", "bytes_in_flight", "fused_run", "lib", "run", "run_int4"]

@@ -42,7 +42,8 @@ class GemvError(RuntimeError):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
                 ("waves_per_block", ctypes.c_int), ("unroll", ctypes.c_int),
-                ("waves_per_cu", ctypes.c_int), ("mfma", ctypes.c_int)]
+                ("waves_per_cu", ctypes.c_int), ("mfma", ctypes.c_int),
+                ("weights", ctypes.c_int)]
 
 
 class DeviceDesc(ctypes.Structure):
@@ -59,7 +60,8 @@ class PlanInfo(ctypes.Structure):
                 ("bytes_in_flight_needed", ctypes.c_double), ("waves_per_cu", ctypes.c_int),
                 ("lds_bytes", ctypes.c_int), ("mfma", ctypes.c_int),
                 ("mfma_splits", ctypes.c_int), ("mfma_slice", ctypes.c_int64),
-                ("mfma_grid_x", ctypes.c_int), ("mfma_depth_bound", ctypes.c_int)]
+                ("mfma_grid_x", ctypes.c_int), ("mfma_depth_bound", ctypes.c_int),
+                ("weights", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -91,6 +93,7 @@ SIGNATURES = {
     "gemv_plan_destroy": (None, [_P]),
     "gemv_run": (_INT, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _SZ, _P]),
     "gemv_fused_run": (_INT, [_P, ctypes.POINTER(Segment), _INT, _P, _I64, _P, _SZ, _P]),
+    "gemv_int4_run": (_INT, [_P, _P, _I64, _P, _I64, _P, _P, _P]),
     "gemv_graph_begin": (_INT, [_P]),
     "gemv_graph_end": (_INT, [_P, ctypes.POINTER(_P)]),
     "gemv_graph_launch": (_INT, [_P, _P]),
@@ -133,9 +136,13 @@ def bytes_in_flight(bytes_per_s: float, latency_s: float) -> float:
     return float(_lib.gemv_bytes_in_flight(bytes_per_s, latency_s))
 
 
-def _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu=0, mfma=0):
+WEIGHTS = {"bf16": 0, "int4": 1}
+
+
+def _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu=0, mfma=0,
+          weights="bf16"):
     return PlanOpts(int(splits), int(rows_per_wave), int(waves_per_block), int(unroll),
-                    int(waves_per_cu), int(mfma))
+                    int(waves_per_cu), int(mfma), WEIGHTS[weights])
 
 
 class Plan:
@@ -147,9 +154,11 @@ class Plan:
 
     def __init__(self, n: int, k: int, m: int = 1, device=None, *, splits: int = 0,
                  rows_per_wave: int = 0, waves_per_block: int = 0, unroll: int = 0,
-                 waves_per_cu: int = 0, mfma: int = 0, desc: tuple | None = None):
+                 waves_per_cu: int = 0, mfma: int = 0, weights: str = "bf16",
+                 desc: tuple | None = None):
         self._h = ctypes.c_void_p()
-        opts = _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu, mfma)
+        opts = _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu, mfma,
+                     weights)
         if desc is not None:
             d = DeviceDesc(int(desc[0]), float(desc[1]), float(desc[2]))
             st = _lib.gemv_plan_for(ctypes.byref(self._h), n, k, m, ctypes.byref(d),
@@ -229,6 +238,21 @@ def run(plan: Plan, W: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
                        _row_stride(X, "X"), Y.data_ptr(), _row_stride(Y, "Y"), ws_ptr,
                        ws_bytes, _stream_handle(stream))
     _check(st, "gemv_run")
+    return Y
+
+
+def run_int4(plan: Plan, Wq: torch.Tensor, S: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
+             stream=None) -> torch.Tensor:
+    """Y = X . W^T for INT4 weights (plan made with weights="int4"): Wq uint8 [n, ldq]
+    packed nibbles, S bf16 [n, lds] group scales, X bf16 [k] or [1, k], Y fp32 [n] or
+    [1, n]. Returns Y."""
+    if Wq.dtype != torch.uint8 or S.dtype != torch.bfloat16 or X.dtype != torch.bfloat16 or \
+            Y.dtype != torch.float32:
+        raise TypeError("Wq must be uint8, S and X bfloat16, Y float32")
+    st = _lib.gemv_int4_run(plan.handle, Wq.data_ptr(), _row_stride(Wq, "Wq"), S.data_ptr(),
+                            _row_stride(S, "S"), X.data_ptr(), Y.data_ptr(),
+                            _stream_handle(stream))
+    _check(st, "gemv_int4_run")
     return Y
 
 

@@ -557,7 +557,8 @@ bool aligned2(const void *p) { return ((uintptr_t)p & 1u) == 0; }
 gemv_status validate(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
                      int64_t ldx, void *ws, size_t ws_bytes)
 {
-    if (!p || !segs || nseg < 1 || nseg > GEMV_MAX_SEGMENTS || !X)
+    if (!p || !segs || nseg < 1 || nseg > GEMV_MAX_SEGMENTS || !X ||
+        p->weights != GEMV_WEIGHTS_BF16)
         return GEMV_ERR_INVALID_ARG;
     if (p->m > 1 && ldx < p->k)
         return GEMV_ERR_INVALID_ARG;
@@ -744,6 +745,19 @@ extern "C" gemv_status gemv_run(gemv_plan_t p, const void *W, int64_t ldw, const
         return GEMV_ERR_INVALID_ARG;
     gemv_segment seg = {W, p->n, ldw, Y, ldy};
     return launch(p, &seg, 1, X, ldx, workspace, ws_bytes, stream);
+}
+
+extern "C" gemv_status gemv_int4_run(gemv_plan_t p, const void *Wq, int64_t ldq, const void *S,
+                                     int64_t lds, const void *X, float *Y, void *stream)
+{
+    if (!p || !Wq || !S || !X || !Y || p->weights != GEMV_WEIGHTS_INT4)
+        return GEMV_ERR_INVALID_ARG;
+    const int64_t groups = (p->k + kInt4Group - 1) / kInt4Group;
+    if (ldq < p->k / 2 || ldq % 16 != 0 || ldq > INT32_MAX || lds < groups || lds > INT32_MAX)
+        return GEMV_ERR_INVALID_ARG;
+    if (!aligned16(Wq) || !aligned16(X) || !aligned2(S) || !aligned4(Y))
+        return GEMV_ERR_MISALIGNED;
+    return bbd::launch_int4(p, Wq, ldq, S, lds, X, Y, stream);
 }
 
 extern "C" gemv_status gemv_fused_run(gemv_plan_t p, const gemv_segment *segs, int nseg,

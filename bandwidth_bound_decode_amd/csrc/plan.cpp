@@ -149,6 +149,86 @@ int mfma_depth_for(int64_t slice, int s)
 
 bool valid_waves(int w) { return w == 1 || w == 2 || w == 4 || w == 8; }
 
+// INT4 weights, unsplit. A product of a 32-weight vector passes through its 16-step dot2
+// chain (+1 inside the first dot2), the scaled addition into the lane's accumulator, one
+// more such addition per later vector of the lane, and the 6 levels of the wave reduction.
+int int4_depth_for(int64_t k)
+{
+    int64_t vecs = ceil_div(k, kInt4VecElems);
+    return (int)(17 + 1 + ceil_div(vecs, kWaveLanes) + 6);
+}
+
+bool int4_tile_supported(int u, int r)
+{
+    return (r == 1 && (u == 1 || u == 2 || u == 4)) || (r == 2 && (u == 1 || u == 2));
+}
+
+// Tiles measured on MI355X (probe sweep at 4096x14336, 6144x4096, 28672x4096): x staged in
+// LDS whenever it fits; rows of 4 or more wave steps one per wave in bursts of 4, 8 waves
+// per workgroup; shorter rows two per wave (each x vector serves both) in bursts of 2, 4
+// waves per workgroup. Without LDS, two rows per single-wave workgroup.
+gemv_status plan_int4(gemv_plan_t *out, int64_t n, int64_t k, int m,
+                      const gemv_device_desc *dev, const gemv_plan_opts &o)
+{
+    if (m != 1 || k % kInt4VecElems != 0 || o.splits > 1 || o.mfma > 0 || o.waves_per_cu != 0)
+        return GEMV_ERR_INVALID_ARG;
+    const int64_t vecs = k / kInt4VecElems;
+    const int64_t steps = ceil_div(vecs, kWaveLanes);
+    const bool xlds = 2 * k <= kInt4MaxLdsX;
+    int r, u, waves;
+    if (xlds && steps >= 4) {
+        r = 1;
+        u = 4;
+        waves = 8;
+    } else if (xlds) {
+        r = 2;
+        u = steps >= 2 ? 2 : 1;
+        waves = 4;
+    } else {
+        r = 2;
+        u = 2;
+        waves = 1;
+    }
+    if (o.rows_per_wave)
+        r = o.rows_per_wave;
+    if (o.unroll)
+        u = o.unroll;
+    if (o.waves_per_block)
+        waves = o.waves_per_block;
+    if (!int4_tile_supported(u, r) || !valid_waves(waves))
+        return GEMV_ERR_INVALID_ARG;
+    const int depth = int4_depth_for(k);
+    if (depth > kMaxDepth)
+        return GEMV_ERR_INVALID_ARG;
+    gemv_plan_s *p = new (std::nothrow) gemv_plan_s;
+    if (!p)
+        return GEMV_ERR_INVALID_ARG;
+    memset(p, 0, sizeof *p);
+    p->n = n;
+    p->k = k;
+    p->m = 1;
+    p->device = -1;
+    p->dev = *dev;
+    p->splits = 1;
+    p->rows_per_wave = r;
+    p->waves_per_block = waves;
+    p->unroll = u;
+    p->slice = k;
+    p->grid_x = (int)ceil_div(n, (int64_t)r * waves);
+    p->grid_y = 1;
+    p->block_threads = kWaveLanes * waves;
+    p->depth_bound = depth;
+    p->weights = GEMV_WEIGHTS_INT4;
+    p->lds_bytes = xlds ? (int)(2 * k) : 0;   // the staged x
+    int64_t per_cu = ceil_div((int64_t)p->grid_x * waves, dev->compute_units);
+    if (per_cu > kMaxWavesPerCU)
+        per_cu = kMaxWavesPerCU;
+    p->bif_per_cu = (double)per_cu * u * r * kWaveLanes * 16.0;
+    p->bif_needed = gemv_bytes_in_flight(dev->hbm_bytes_per_s, dev->latency_s) / dev->compute_units;
+    *out = p;
+    return GEMV_OK;
+}
+
 }  // namespace
 
 extern "C" double gemv_bytes_in_flight(double bytes_per_s, double latency_s)
@@ -169,11 +249,15 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     // Row indices and grid sizes are held in 32 bits on the device.
     if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30)
         return GEMV_ERR_INVALID_ARG;
-    gemv_plan_opts o = {0, 0, 0, 0, 0, 0};
+    gemv_plan_opts o = {0, 0, 0, 0, 0, 0, 0};
     if (opts)
         o = *opts;
     if (o.splits < 0 || o.rows_per_wave < 0 || o.waves_per_block < 0 || o.unroll < 0 ||
         o.waves_per_cu < -1 || o.waves_per_cu > kMaxWavesPerCU || o.mfma < -1 || o.mfma > 1)
+        return GEMV_ERR_INVALID_ARG;
+    if (o.weights == GEMV_WEIGHTS_INT4)
+        return plan_int4(out, n, k, m, dev, o);
+    if (o.weights != GEMV_WEIGHTS_BF16)
         return GEMV_ERR_INVALID_ARG;
 
     int r, u, waves;
@@ -352,6 +436,7 @@ extern "C" gemv_status gemv_plan_query(gemv_plan_t p, gemv_plan_info *info)
     info->mfma_slice = p->mfma_slice;
     info->mfma_grid_x = p->mfma_grid_x;
     info->mfma_depth_bound = p->mfma_depth;
+    info->weights = p->weights;
     return GEMV_OK;
 }
 

@@ -42,6 +42,10 @@ constexpr int kMfmaRowsPerBlock = 32;
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaChunk = 64;
 constexpr int kMfmaMinBatch = 8;
+// INT4 weights (int4.hip): 32 weights per 16-byte vector, one bf16 scale per 128.
+constexpr int kInt4VecElems = 32;
+constexpr int kInt4Group = 128;
+constexpr int kInt4MaxLdsX = 64 * 1024;   // x staged in LDS up to this many bytes (2K)
 
 // One compiled (M, R, U) combination of the aligned fast-path kernel. The unaligned path
 // exists for every M and takes R at run time.
@@ -81,6 +85,11 @@ gemv_status launch_batch(gemv_plan_t p, const gemv_segment *segs, int nseg, cons
 gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
                         int64_t ldx, void *ws, void *stream, bool *done);
 
+// INT4-weight launch (int4.hip) of a validated call; the plan's unroll, rows per wave and
+// LDS size pick the kernel.
+gemv_status launch_int4(gemv_plan_t p, const void *Wq, int64_t ldq, const void *S, int64_t lds,
+                        const void *X, float *Y, void *stream);
+
 // Record the HIP error code behind a GEMV_ERR_DEVICE / GEMV_ERR_CAPTURE for
 // gemv_last_hip_error() (thread-local) and return `status`.
 gemv_status record_hip_error(int hip_error, gemv_status status);
@@ -109,4 +118,5 @@ struct gemv_plan_s {
     int64_t mfma_slice;
     int mfma_grid_x;
     int mfma_depth;
+    int weights;                // GEMV_WEIGHTS_BF16 or GEMV_WEIGHTS_INT4
 };

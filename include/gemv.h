@@ -87,7 +87,12 @@ typedef struct {
     int unroll;
     int waves_per_cu;
     int mfma;
+    int weights;        /* GEMV_WEIGHTS_BF16 (0) or GEMV_WEIGHTS_INT4; see gemv_int4_run */
 } gemv_plan_opts;
+
+/* Weight formats a plan can be made for. */
+#define GEMV_WEIGHTS_BF16 0
+#define GEMV_WEIGHTS_INT4 1
 
 /*
  * The device a plan is sized for. gemv_plan fills it from the runtime; gemv_plan_for takes
@@ -124,6 +129,7 @@ typedef struct {
     int64_t mfma_slice;     /* K elements per slice, a multiple of 64 */
     int mfma_grid_x;        /* 32-row blocks: ceil(N / 32); 8 waves per workgroup */
     int mfma_depth_bound;   /* h for that kernel, counting 32 roundings per MFMA */
+    int weights;            /* the plan's weight format */
 } gemv_plan_info;
 
 /*
@@ -204,6 +210,31 @@ typedef struct {
 gemv_status gemv_fused_run(gemv_plan_t p, const gemv_segment *segs, int nseg,
                            const void *X, int64_t ldx,
                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Batch-1 GEMV with INT4 weights (decode-GEMV page, the follow-up in which the weights
+ * become INT4: a quarter of the bytes, unpacked in registers while the next loads are in
+ * flight). The page fixes no format; this library's:
+ *   - weight v in [-8, 7] stored as a two's-complement nibble; row n of Wq starts at
+ *     Wq + n*ldq bytes, and element k is the low nibble of byte k/2 when k is even and
+ *     the high nibble when k is odd;
+ *   - one bf16 scale per run of 128 consecutive elements of a row: scale[n][k/128] at
+ *     S + n*lds (elements);
+ *   - the weight's value is v * scale, and Y[n] = sum_k (v_nk * scale[n][k/128]) * X[k],
+ *     accumulated in fp32 and overwritten, within the same tolerance as gemv_run.
+ * The plan must come from gemv_plan / gemv_plan_for with opts.weights = GEMV_WEIGHTS_INT4,
+ * m = 1 and k a multiple of 32 (whole 16-byte vectors; the last group may be short); it
+ * never splits K, and opts.splits > 1, waves_per_cu and mfma = 1 are GEMV_ERR_INVALID_ARG.
+ * rows_per_wave (1 or 2), unroll (1, 2 or 4; 1 or 2 with two rows) and waves_per_block may
+ * be forced.
+ * Wq and X must be 16-byte aligned with ldq a multiple of 16 (>= k/2), S 2-byte and Y
+ * 4-byte aligned (else GEMV_ERR_MISALIGNED); lds >= ceil(k/128); leading dimensions up
+ * to 2^31 - 1. No workspace; no allocation or host synchronisation (capture-safe).
+ * gemv_run and gemv_fused_run reject INT4 plans, and this call rejects bf16 plans
+ * (GEMV_ERR_INVALID_ARG).
+ */
+gemv_status gemv_int4_run(gemv_plan_t p, const void *Wq, int64_t ldq, const void *S,
+                          int64_t lds, const void *X, float *Y, void *stream);
 
 /*
  * Graph capture of a GEMV sequence, so a whole decode step crosses the host-device boundary

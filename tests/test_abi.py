@@ -20,7 +20,7 @@ FAKE = 0x7F0000000000          # 16-byte aligned stand-in for a device address (
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gemv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():

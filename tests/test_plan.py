@@ -244,3 +244,33 @@ def test_mfma_plans():
     assert long_k["mfma"] == 1 and long_k["mfma_depth_bound"] <= 160
     with pytest.raises(bbd.GemvError):
         plan(4096, 14336, 16, mfma=2)
+
+
+def test_int4_plans():
+    """INT4 weights: batch 1, whole 32-weight vectors, no split and no workspace; x staged in
+    LDS when it fits; long rows one per wave in bursts of 4, short rows two per wave."""
+    i = plan(4096, 14336, weights="int4").info
+    assert i["weights"] == 1 and i["splits"] == 1 and i["mfma"] == 0
+    assert (i["rows_per_wave"], i["unroll"], i["waves_per_block"]) == (1, 4, 8)
+    assert (i["grid_x"], i["grid_y"], i["block_threads"], i["lds_bytes"]) == (512, 1, 512, 28672)
+    # 16 dot2 steps + 1, the scaled addition, 7 vectors per lane, 6 wave levels
+    assert i["depth_bound"] == 17 + 1 + 7 + 6
+    assert plan(4096, 14336, weights="int4").workspace_size == 0
+    g = plan(28672, 4096, weights="int4").info
+    assert (g["rows_per_wave"], g["unroll"], g["waves_per_block"], g["grid_x"]) == (2, 2, 4, 3584)
+    assert plan(7, 32, weights="int4").info["unroll"] == 1
+    big = plan(64, 65536, weights="int4").info                 # 128 KiB of x: no LDS
+    assert (big["lds_bytes"], big["rows_per_wave"], big["waves_per_block"]) == (0, 2, 1)
+    f = plan(7, 4128, weights="int4", unroll=1, rows_per_wave=2, waves_per_block=2).info
+    assert (f["unroll"], f["rows_per_wave"], f["waves_per_block"], f["grid_x"]) == (1, 2, 2, 2)
+    assert plan(4096, 14336).info["weights"] == 0
+    for bad in (dict(k=100), dict(m=2), dict(splits=2), dict(unroll=3), dict(unroll=8),
+                dict(rows_per_wave=4), dict(rows_per_wave=2, unroll=4), dict(waves_per_cu=8),
+                dict(waves_per_block=3), dict(mfma=1)):
+        args = dict(n=64, k=4096, m=1)
+        args.update({k: v for k, v in bad.items() if k in args})
+        opts = {k: v for k, v in bad.items() if k not in args}
+        with pytest.raises(bbd.GemvError):
+            plan(args["n"], args["k"], args["m"], weights="int4", **opts)
+    with pytest.raises(bbd.GemvError):
+        plan(64, 1 << 20, weights="int4")           # depth bound

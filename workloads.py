@@ -135,3 +135,41 @@ def draw_decode_step(device: str | torch.device = "cuda", layers: int = LAYERS,
             parts = [w]
         out.append((g, parts, x))
     return out
+
+
+# --------------------------------------------------------------------------- INT4 weights
+INT4_GROUP = 128
+
+
+def draw_int4(n: int, k: int, gen: torch.Generator, device: str | torch.device = "cpu",
+              ldq: int | None = None, lds: int | None = None):
+    """Seeded INT4 weights in the packed format the INT4 GEMV reads, drawn the way a weight
+    of the workloads above would be quantized: W ~ N(0, SIGMA_W) in bf16, then per row and
+    run of 128 elements a bf16 scale absmax / 7 and integers round(W / scale) clamped to
+    [-8, 7]. This only prepares inputs; the GEMV's own arithmetic (dequantize, multiply,
+    sum) is not here.
+
+    Returns (packed uint8 [n, ldq], bf16 scales [n, lds], the integer values int8 [n, k]):
+    element k of a row is the low nibble of byte k/2 when k is even and the high nibble when
+    odd, two's complement; padding bytes and scales beyond the last group are filled with
+    0xEE / NaN so a read of them shows.
+    """
+    groups = (k + INT4_GROUP - 1) // INT4_GROUP
+    ldq = (k + 1) // 2 if ldq is None else ldq
+    lds = groups if lds is None else lds
+    assert ldq >= (k + 1) // 2 and lds >= groups
+    w = bf16_normal((n, k), SIGMA_W, gen, device).float()
+    pad = groups * INT4_GROUP - k
+    wg = torch.nn.functional.pad(w, (0, pad)).view(n, groups, INT4_GROUP)
+    scale = (wg.abs().amax(dim=2) / 7.0).to(torch.bfloat16)
+    scale = torch.where(scale == 0, torch.ones_like(scale), scale)
+    q = torch.round(wg / scale.float()[:, :, None]).clamp_(-8, 7).view(n, -1)[:, :k]
+    q = q.to(torch.int8)
+    nib = (q.to(torch.int16) & 0xF).to(torch.uint8)
+    if k % 2:
+        nib = torch.nn.functional.pad(nib, (0, 1))
+    packed = torch.full((n, ldq), 0xEE, dtype=torch.uint8, device=device)
+    packed[:, :(k + 1) // 2] = nib[:, 0::2] | (nib[:, 1::2] << 4)
+    scales = torch.full((n, lds), float("nan"), dtype=torch.bfloat16, device=device)
+    scales[:, :groups] = scale
+    return packed, scales, q
