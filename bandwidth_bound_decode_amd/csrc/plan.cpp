@@ -163,10 +163,10 @@ bool int4_tile_supported(int u, int r)
     return (r == 1 && (u == 1 || u == 2 || u == 4)) || (r == 2 && (u == 1 || u == 2));
 }
 
-// Tiles measured on MI355X (probe sweep at 4096x14336, 6144x4096, 28672x4096): x staged in
-// LDS whenever it fits; rows of 4 or more wave steps one per wave in bursts of 4, 8 waves
-// per workgroup; shorter rows two per wave (each x vector serves both) in bursts of 2, 4
-// waves per workgroup. Without LDS, two rows per single-wave workgroup.
+// Tiles measured on MI355X (sweep at the six Llama shapes): x staged in LDS whenever it
+// fits, 8 waves per workgroup; rows of 4 or more wave steps one per wave in bursts of 4;
+// shorter rows in bursts of 2, two per wave (each x vector serves both) once N reaches
+// 16384 rows, one per wave below that. Without LDS, two rows per single-wave workgroup.
 gemv_status plan_int4(gemv_plan_t *out, int64_t n, int64_t k, int m,
                       const gemv_device_desc *dev, const gemv_plan_opts &o)
 {
@@ -181,9 +181,9 @@ gemv_status plan_int4(gemv_plan_t *out, int64_t n, int64_t k, int m,
         u = 4;
         waves = 8;
     } else if (xlds) {
-        r = 2;
+        r = n >= kInt4TwoRowsFrom ? 2 : 1;
         u = steps >= 2 ? 2 : 1;
-        waves = 4;
+        waves = 8;
     } else {
         r = 2;
         u = 2;

@@ -46,6 +46,7 @@ constexpr int kMfmaMinBatch = 8;
 constexpr int kInt4VecElems = 32;
 constexpr int kInt4Group = 128;
 constexpr int kInt4MaxLdsX = 64 * 1024;   // x staged in LDS up to this many bytes (2K)
+constexpr int64_t kInt4TwoRowsFrom = 16384;   // short INT4 rows: two per wave from this N
 
 // One compiled (M, R, U) combination of the aligned fast-path kernel. The unaligned path
 // exists for every M and takes R at run time.

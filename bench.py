@@ -195,6 +195,42 @@ def bench_gemv(torch, bbd, g, w, x, steps, warmup, segments=(), **plan_opts):
     return res, total, per, plan
 
 
+def bench_int4(torch, bbd, workloads, name, n, k, steps, warmup):
+    """Rotated timing of one INT4-weight GEMV (batch 1): per-launch event pairs and the same
+    launches back to back from one graph. Algorithmic bytes: packed weights, scales, x, y."""
+    gen = workloads.generator(2000 + n % 997, "cuda")
+    packed, scales, _ = workloads.draw_int4(n, k, gen, "cuda")
+    x = workloads.bf16_normal((1, k), workloads.SIGMA_X, gen, "cuda")
+    unit = packed.numel() + scales.numel() * 2
+    copies = max(2, math.ceil(ROTATION_BYTES / unit) + 1)
+    wa = torch.empty((copies,) + tuple(packed.shape), dtype=packed.dtype, device="cuda")
+    sa = torch.empty((copies,) + tuple(scales.shape), dtype=scales.dtype, device="cuda")
+    for i in range(copies):
+        wa[i].copy_(packed)
+        sa[i].copy_(scales)
+    plan = bbd.Plan(n, k, 1, weights="int4")
+    Y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch(i, stream=None):
+        bbd.run_int4(plan, wa[i % copies], sa[i % copies], x, Y, stream)
+    _, per = time_launches(torch, launch, steps, warmup, stream)
+    side = torch.cuda.Stream()
+    total = time_graph(torch, lambda i: launch(i, side), steps, side)
+    nb = unit + 2 * k + 4 * n
+    info = plan.info
+    res = {"name": name, "weights": "int4", "shape": f"{n}x{k}", "m": 1, "alg_bytes": nb,
+           "plan": {key: info[key] for key in ("rows_per_wave", "unroll", "waves_per_block",
+                                               "grid_x", "lds_bytes")},
+           "rotation_copies": copies, "us_median": statistics.median(per) * 1e6,
+           "us_per_step_back_to_back": total / steps * 1e6,
+           "TBps_median": nb / statistics.median(per) / 1e12,
+           "TBps_back_to_back": nb * steps / total / 1e12}
+    res["pct_peak_back_to_back"] = 100 * res["TBps_back_to_back"] * 1e12 / PEAK_HBM
+    del wa, sa
+    return res
+
+
 def bench_decode_step(torch, bbd, workloads, replays, warmup):
     """The 129-GEMV decode step three ways: eager launches, one graph of the 129 launches,
     and one graph holding the single persistent chain launch."""
@@ -376,6 +412,17 @@ def main(argv=None):
                     r[k] = round(r[k], 3)
             log(f"{name}: {r['us_median']:.2f} us, {r['TBps_median']:.3f} TB/s")
             out.setdefault("shapes", []).append(r)
+        # INT4 weights at the same projection shapes (batch 1)
+        for name, n, k in (("int4_down", 4096, 14336), ("int4_k_proj", 1024, 4096),
+                           ("int4_o_proj", 4096, 4096), ("int4_qkv", 6144, 4096),
+                           ("int4_gate_up", 28672, 4096), ("int4_lm_head", workloads.VOCAB, 4096)):
+            r = bench_int4(torch, bbd, workloads, name, n, k, args.shape_steps, 10)
+            for key in list(r):
+                if isinstance(r[key], float):
+                    r[key] = round(r[key], 3)
+            log(f"{name}: {r['us_per_step_back_to_back']:.2f} us back to back, "
+                f"{r['TBps_back_to_back']:.3f} TB/s")
+            out.setdefault("int4_shapes", []).append(r)
 
     if not args.skip_decode:
         d = bench_decode_step(torch, bbd, workloads, args.decode_replays, 3)

@@ -257,7 +257,9 @@ def test_int4_plans():
     assert i["depth_bound"] == 17 + 1 + 7 + 6
     assert plan(4096, 14336, weights="int4").workspace_size == 0
     g = plan(28672, 4096, weights="int4").info
-    assert (g["rows_per_wave"], g["unroll"], g["waves_per_block"], g["grid_x"]) == (2, 2, 4, 3584)
+    assert (g["rows_per_wave"], g["unroll"], g["waves_per_block"], g["grid_x"]) == (2, 2, 8, 1792)
+    q = plan(6144, 4096, weights="int4").info
+    assert (q["rows_per_wave"], q["unroll"], q["waves_per_block"], q["grid_x"]) == (1, 2, 8, 768)
     assert plan(7, 32, weights="int4").info["unroll"] == 1
     big = plan(64, 65536, weights="int4").info                 # 128 KiB of x: no LDS
     assert (big["lds_bytes"], big["rows_per_wave"], big["waves_per_block"]) == (0, 2, 1)
