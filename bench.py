@@ -231,6 +231,48 @@ def bench_int4(torch, bbd, workloads, name, n, k, steps, warmup):
     return res
 
 
+def bench_decode_step_int4(torch, bbd, workloads, replays):
+    """The same 129-GEMV decode step with INT4 weights: every projection (QKV and gate_up as
+    one row-concatenated matrix each) through gemv_int4_run, captured in one graph, in stream
+    order. Weights are drawn freshly (about 3.8 GB packed), so the first replay finds none of
+    them in cache and later replays find at most the last ~256 MB."""
+    gen = workloads.generator(3000, "cuda")
+    plans, steps, nb = {}, [], 0
+    for g in workloads.decode_step_gemvs():
+        packed, scales, _ = workloads.draw_int4(g.n, g.k, gen, "cuda")
+        x = workloads.bf16_normal((1, g.k), workloads.SIGMA_X, gen, "cuda")
+        y = torch.empty((1, g.n), dtype=torch.float32, device="cuda")
+        if (g.n, g.k) not in plans:
+            plans[(g.n, g.k)] = bbd.Plan(g.n, g.k, 1, weights="int4")
+        steps.append((plans[(g.n, g.k)], packed, scales, x, y))
+        nb += packed.numel() + scales.numel() * 2 + 2 * g.k + 4 * g.n
+    stream = torch.cuda.Stream()
+    graph = bbd.Graph(stream)
+    with torch.cuda.stream(stream):
+        with graph:
+            for plan, packed, scales, x, y in steps:
+                bbd.run_int4(plan, packed, scales, x, y, stream)
+    for _ in range(3):
+        graph.launch(stream)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.launch(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / 1e3)
+    graph.destroy()
+    t = statistics.median(times)
+    return {"gemvs": len(steps), "alg_bytes": nb, "replays": replays,
+            "graph_ms_median": t * 1e3, "graph_TBps": nb / t / 1e12,
+            "graph_mbu": nb / t / PEAK_HBM,
+            "note": "INT4 weights (signed nibbles, bf16 scale per 128), batch 1, one graph of "
+                    "129 gemv_int4_run launches; QKV and gate_up as one row-concatenated matrix"}
+
+
 def bench_decode_step(torch, bbd, workloads, replays, warmup):
     """The 129-GEMV decode step three ways: eager launches, one graph of the 129 launches,
     and one graph holding the single persistent chain launch."""
@@ -434,6 +476,14 @@ def main(argv=None):
             f"(MBU {d['chain_graph_mbu']:.3f}); graph of 129 launches "
             f"{d['graph_ms_median']:.3f} ms (MBU {d['graph_mbu']:.3f}); eager "
             f"{d['eager_ms_median']:.3f} ms")
+        torch.cuda.empty_cache()
+        d4 = bench_decode_step_int4(torch, bbd, workloads, args.decode_replays)
+        for k in list(d4):
+            if isinstance(d4[k], float):
+                d4[k] = round(d4[k], 4)
+        out["decode_step_int4"] = d4
+        log(f"decode step, INT4 weights: graph of 129 launches {d4['graph_ms_median']:.3f} ms "
+            f"({d4['graph_TBps']:.3f} TB/s, MBU {d4['graph_mbu']:.3f})")
 
     print(json.dumps(out), flush=True)
     return 0
