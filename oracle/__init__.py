@@ -47,6 +47,10 @@ def _bind(so):
     so.oracle_bf16_to_f64.restype = None
     so.oracle_gemv_f64.argtypes = [p, i64, i64, i64, p, i64, i64, p, p, ctypes.c_int]
     so.oracle_gemv_f64.restype = ctypes.c_int
+    if hasattr(so, "oracle_gemv_rmsnorm_f64"):
+        so.oracle_gemv_rmsnorm_f64.argtypes = [p, i64, i64, i64, p, p, ctypes.c_double, p, p,
+                                               ctypes.c_int]
+        so.oracle_gemv_rmsnorm_f64.restype = ctypes.c_int
     if hasattr(so, "oracle_gemv_q4_f64"):
         so.oracle_q4_dequant_f64.argtypes = [p, i64, i64, i64, p, i64, p]
         so.oracle_q4_dequant_f64.restype = ctypes.c_int
@@ -156,6 +160,29 @@ def gemv_q4(wq, scales, x_bits, nthreads: int = 0, so=None):
                                m, ldx, y.ctypes.data, s.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError("oracle_gemv_q4_f64 rejected its arguments")
+    return y, s
+
+
+def gemv_rmsnorm(w_bits, h_bits, gamma_bits, eps: float, nthreads: int = 0, so=None):
+    """y_ref, s_abs for y = rms_inv * W . (gamma * h), rms_inv = 1/sqrt(mean(h^2) + eps);
+    W bf16 [n, >=k] (row-strided allowed), h and gamma bf16 [k]. float64 arrays [1, n]."""
+    so = so or lib()
+    w = _u16(w_bits)
+    h = np.ascontiguousarray(_u16(h_bits)).ravel()
+    g = np.ascontiguousarray(_u16(gamma_bits)).ravel()
+    k = h.size
+    if w.ndim != 2 or w.shape[1] < k or g.size != k:
+        raise ValueError("W must be 2-D with >= k columns and gamma as long as h")
+    n = w.shape[0]
+    if w.shape[1] > 1 and w.strides[1] != 2:
+        raise ValueError("rows must be contiguous")
+    ldw = w.strides[0] // 2 if n > 1 else max(w.shape[1], 1)
+    y = np.empty((1, n), dtype=np.float64)
+    s = np.empty((1, n), dtype=np.float64)
+    rc = so.oracle_gemv_rmsnorm_f64(w.ctypes.data, n, k, ldw, h.ctypes.data, g.ctypes.data,
+                                    float(eps), y.ctypes.data, s.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gemv_rmsnorm_f64 rejected its arguments")
     return y, s
 
 

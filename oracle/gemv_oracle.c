@@ -164,3 +164,46 @@ int oracle_gemv_q4_f64(const uint8_t *Wq, int64_t N, int64_t K, int64_t ldq,
     }
     return 0;
 }
+
+/*
+ * RMSNorm prologue. The GPU performance chains page ("Fused RMSNorm traffic") notes that at
+ * decode batch 1 a normalisation moves trivial bytes and costs its launches; fused into the
+ * projection that consumes it (QKV, gate_up), those launches disappear. The pages do not
+ * write the normalisation out; this is the usual RMSNorm (mean of squares plus eps, inverse
+ * square root, per-element gain gamma) followed by the GEMV, with no rounding in between:
+ *   rms_inv = 1 / sqrt( (1/K) * sum_k h_k^2 + eps )
+ *   y[n]    = rms_inv * sum_k W[n][k] * (gamma_k * h_k)
+ * with h (the residual-stream vector), gamma and W in bf16 and eps >= 0. The products
+ * h_k^2 and W*gamma*h are exact in fp64 (at most 24 significant bits); the sums run in
+ * k-ascending order; the square root and the divisions are IEEE fp64. Sabs holds
+ * rms_inv * sum_k |W[n][k] * gamma_k * h_k|, the magnitude the tolerance scales with.
+ * Returns 0, or -1 for a bad argument.
+ */
+int oracle_gemv_rmsnorm_f64(const uint16_t *W, int64_t N, int64_t K, int64_t ldw,
+                            const uint16_t *H, const uint16_t *G, double eps,
+                            double *Y, double *Sabs, int nthreads)
+{
+    if (!W || !H || !G || !Y || !Sabs || N < 0 || K < 1 || ldw < K || !(eps >= 0.0))
+        return -1;
+    double squares = 0.0;
+    for (int64_t i = 0; i < K; i++) {
+        const double hv = bf16_value(H[i]);
+        squares += hv * hv;
+    }
+    const double rms_inv = 1.0 / sqrt(squares / (double)K + eps);
+    int threads = oracle_threads(nthreads);
+    (void)threads;
+#pragma omp parallel for schedule(static) num_threads(threads)
+    for (int64_t row = 0; row < N; ++row) {
+        const uint16_t *wrow = W + row * ldw;
+        double dot = 0.0, size = 0.0;
+        for (int64_t i = 0; i < K; i++) {
+            const double part = bf16_value(wrow[i]) * (bf16_value(G[i]) * bf16_value(H[i]));
+            dot += part;
+            size += fabs(part);
+        }
+        Y[row] = rms_inv * dot;
+        Sabs[row] = rms_inv * size;
+    }
+    return 0;
+}

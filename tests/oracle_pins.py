@@ -268,9 +268,71 @@ def pin_q4_brute_force(so):
     assert not y.any() and not s.any(), "all-zero weights"
 
 
+# --------------------------------------------------------------------------- RMSNorm prologue
+def pin_rmsnorm_unit_scale_is_plain_gemv(so):
+    """gamma = 1 and eps chosen so that mean(h^2) + eps = 1 exactly: rms_inv = 1 and the
+    result must be the (separately pinned) plain GEMV bit for bit."""
+    rng = np.random.default_rng(41)
+    k = 256
+    h = _bf16_bits(rng.choice([-1.0, -0.5, 0.5, 1.0], size=k))   # h^2 in {1/4, 1}
+    hv = oracle.bf16_to_f64(h, so=so)
+    mean = float(np.sum(hv * hv)) / k                          # exact: a multiple of 1/1024
+    eps = 1.0 - mean
+    assert 0.0 <= eps < 1.0
+    w = _rand_bits(rng, (9, k + 3), 0.02)[:, :k]
+    gain = _bf16_bits(np.ones(k))
+    y, s = oracle.gemv_rmsnorm(w, h, gain, eps, so=so)
+    y0, s0 = oracle.gemv(w, h, so=so)
+    assert np.array_equal(y, y0) and np.array_equal(s, s0), "rms_inv = 1 must give the GEMV"
+
+
+def pin_rmsnorm_closed_forms(so):
+    """Constant h = c with eps = 0 gives rms_inv = 1/|c|; a single nonzero h_j = a gives
+    mean(h^2) = a^2 / K; W = I gives y = gamma * h * rms_inv elementwise."""
+    k = 64
+    w = _bf16_bits(np.eye(k))
+    gain = _bf16_bits(np.arange(1, k + 1) / 8.0)
+    h = _bf16_bits(np.full(k, -4.0))
+    y, _ = oracle.gemv_rmsnorm(w, h, gain, 0.0, so=so)
+    gv = oracle.bf16_to_f64(gain, so=so)
+    assert np.array_equal(y[0], gv * -4.0 / 4.0), "constant h"
+    h1 = np.zeros(k)
+    h1[5] = 8.0
+    eps = 0.75                                   # mean = 64/64 = 1, + 0.75 -> rms = sqrt(1.75)
+    y, _ = oracle.gemv_rmsnorm(w, _bf16_bits(h1), gain, eps, so=so)
+    want = np.zeros(k)
+    want[5] = gv[5] * 8.0 * (1.0 / math.sqrt(1.75))
+    assert np.allclose(y[0], want, rtol=1e-15, atol=0), "one nonzero h"
+
+
+def pin_rmsnorm_brute_force(so):
+    """Exact rationals where eps makes mean(h^2) + eps a perfect square s^2: rms_inv = 1/s
+    exactly, so the whole result is rational."""
+    rng = np.random.default_rng(43)
+    n, k = 4, 96
+    w = _rand_bits(rng, (n, k), 0.02)
+    h = _bf16_bits(rng.integers(-8, 9, size=k).astype(np.float64) / 4)
+    gain = _rand_bits(rng, (k,), 1.0)
+    hx = _exact(h)
+    mean = sum(v * v for v in hx) / k
+    root = Fraction(math.ceil(math.sqrt(mean)) + 1)
+    eps = root * root - mean                     # exact in fp64: a multiple of 1/1536 < 2^53
+    assert Fraction(float(eps)) == eps
+    y, s = oracle.gemv_rmsnorm(w, h, gain, float(eps), so=so)
+    gx = _exact(gain)
+    for r in range(n):
+        wx = _exact(w[r])
+        terms = [a * b * c / root for a, b, c in zip(wx, gx, hx)]
+        exact = sum(terms)
+        mag = sum(abs(t) for t in terms)
+        assert abs(Fraction(y[0, r]) - exact) <= Fraction(gamma(k + 4)) * mag, "rmsnorm brute force"
+        assert abs(Fraction(s[0, r]) - mag) <= Fraction(gamma(k + 4)) * mag, "rmsnorm s_abs"
+
+
 PINS = (pin_bf16_decode, pin_identity, pin_one_hot, pin_constant_w, pin_brute_force,
         pin_cancellation, pin_numpy_matmul, pin_thread_invariance, pin_q4_format,
-        pin_q4_equals_bf16_oracle, pin_q4_brute_force)
+        pin_q4_equals_bf16_oracle, pin_q4_brute_force, pin_rmsnorm_unit_scale_is_plain_gemv,
+        pin_rmsnorm_closed_forms, pin_rmsnorm_brute_force)
 
 
 def run_all(lib_path: str) -> int:

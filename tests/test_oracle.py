@@ -83,6 +83,11 @@ MUTATIONS = {
     "q4_ignore_ldq": ("Wq + row * ldq", "Wq + row * ((K + 1) / 2)"),
     "q4_ignore_lds": ("Sc + row * lds", "Sc + row * ((K + 127) / 128)"),
     "q4_abs_without_fabs": ("magnitude += fabs(term);", "magnitude += term;"),
+    "norm_eps_dropped": ("sqrt(squares / (double)K + eps)", "sqrt(squares / (double)K)"),
+    "norm_mean_over_n": ("squares / (double)K", "squares / (double)(N > 0 ? N : 1)"),
+    "norm_gamma_dropped": ("(bf16_value(G[i]) * bf16_value(H[i]))", "bf16_value(H[i])"),
+    "norm_no_sqrt": ("1.0 / sqrt(squares / (double)K + eps)", "1.0 / (squares / (double)K + eps)"),
+    "norm_scale_missing": ("Y[row] = rms_inv * dot;", "Y[row] = dot;"),
 }
 
 
