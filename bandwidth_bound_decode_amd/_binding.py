@@ -43,7 +43,7 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
                 ("waves_per_block", ctypes.c_int), ("unroll", ctypes.c_int),
                 ("waves_per_cu", ctypes.c_int), ("mfma", ctypes.c_int),
-                ("weights", ctypes.c_int)]
+                ("weights", ctypes.c_int), ("prologue", ctypes.c_int)]
 
 
 class DeviceDesc(ctypes.Structure):
@@ -61,7 +61,7 @@ class PlanInfo(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int), ("mfma", ctypes.c_int),
                 ("mfma_splits", ctypes.c_int), ("mfma_slice", ctypes.c_int64),
                 ("mfma_grid_x", ctypes.c_int), ("mfma_depth_bound", ctypes.c_int),
-                ("weights", ctypes.c_int)]
+                ("weights", ctypes.c_int), ("prologue", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -94,6 +94,7 @@ SIGNATURES = {
     "gemv_run": (_INT, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _SZ, _P]),
     "gemv_fused_run": (_INT, [_P, ctypes.POINTER(Segment), _INT, _P, _I64, _P, _SZ, _P]),
     "gemv_int4_run": (_INT, [_P, _P, _I64, _P, _I64, _P, _P, _P]),
+    "gemv_rmsnorm_run": (_INT, [_P, ctypes.POINTER(Segment), _INT, _P, _P, ctypes.c_float, _P]),
     "gemv_graph_begin": (_INT, [_P]),
     "gemv_graph_end": (_INT, [_P, ctypes.POINTER(_P)]),
     "gemv_graph_launch": (_INT, [_P, _P]),
@@ -137,12 +138,13 @@ def bytes_in_flight(bytes_per_s: float, latency_s: float) -> float:
 
 
 WEIGHTS = {"bf16": 0, "int4": 1}
+PROLOGUES = {None: 0, "rmsnorm": 1}
 
 
 def _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu=0, mfma=0,
-          weights="bf16"):
+          weights="bf16", prologue=None):
     return PlanOpts(int(splits), int(rows_per_wave), int(waves_per_block), int(unroll),
-                    int(waves_per_cu), int(mfma), WEIGHTS[weights])
+                    int(waves_per_cu), int(mfma), WEIGHTS[weights], PROLOGUES[prologue])
 
 
 class Plan:
@@ -155,10 +157,10 @@ class Plan:
     def __init__(self, n: int, k: int, m: int = 1, device=None, *, splits: int = 0,
                  rows_per_wave: int = 0, waves_per_block: int = 0, unroll: int = 0,
                  waves_per_cu: int = 0, mfma: int = 0, weights: str = "bf16",
-                 desc: tuple | None = None):
+                 prologue: str | None = None, desc: tuple | None = None):
         self._h = ctypes.c_void_p()
         opts = _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu, mfma,
-                     weights)
+                     weights, prologue)
         if desc is not None:
             d = DeviceDesc(int(desc[0]), float(desc[1]), float(desc[2]))
             st = _lib.gemv_plan_for(ctypes.byref(self._h), n, k, m, ctypes.byref(d),
@@ -254,6 +256,26 @@ def run_int4(plan: Plan, Wq: torch.Tensor, S: torch.Tensor, X: torch.Tensor, Y: 
                             _stream_handle(stream))
     _check(st, "gemv_int4_run")
     return Y
+
+
+def rmsnorm_run(plan: Plan, segments, H: torch.Tensor, gamma: torch.Tensor, eps: float,
+                stream=None):
+    """Y_i = rms_inv * W_i . (gamma * H) for every (W_i, Y_i) in `segments`, with
+    rms_inv = 1/sqrt(mean(H^2) + eps), in one launch (plan made with prologue="rmsnorm").
+    H and gamma bf16 [k] (or [1, k]); W_i bf16 [n_i, >= k] sharing one row stride; Y_i fp32
+    [n_i] (or [1, n_i])."""
+    segs = list(segments)
+    arr = (Segment * max(len(segs), 1))()
+    for i, (w, y) in enumerate(segs):
+        if w.dtype != torch.bfloat16 or y.dtype != torch.float32:
+            raise TypeError("segment W must be bfloat16 and Y float32")
+        arr[i] = Segment(w.data_ptr(), w.shape[0], _row_stride(w, "W"), y.data_ptr(),
+                         w.shape[0])
+    if H.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16:
+        raise TypeError("H and gamma must be bfloat16")
+    st = _lib.gemv_rmsnorm_run(plan.handle, arr, len(segs), H.data_ptr(), gamma.data_ptr(),
+                               float(eps), _stream_handle(stream))
+    _check(st, "gemv_rmsnorm_run")
 
 
 def fused_run(plan: Plan, segments, X: torch.Tensor, workspace: torch.Tensor | None = None,

@@ -29,7 +29,7 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror",
 
 
 RESOURCE_REPORT = os.path.join(LIB_DIR, "kernel_resources.json")
-HIP_UNITS = ("gemv", "whole", "batch", "mfma", "int4", "chain")
+HIP_UNITS = ("gemv", "whole", "batch", "mfma", "int4", "norm", "chain")
 REMARK = "[-Rpass-analysis=kernel-resource-usage]"
 
 

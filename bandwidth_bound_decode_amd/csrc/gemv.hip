@@ -558,7 +558,7 @@ gemv_status validate(gemv_plan_t p, const gemv_segment *segs, int nseg, const vo
                      int64_t ldx, void *ws, size_t ws_bytes)
 {
     if (!p || !segs || nseg < 1 || nseg > GEMV_MAX_SEGMENTS || !X ||
-        p->weights != GEMV_WEIGHTS_BF16)
+        p->weights != GEMV_WEIGHTS_BF16 || p->prologue != 0)
         return GEMV_ERR_INVALID_ARG;
     if (p->m > 1 && ldx < p->k)
         return GEMV_ERR_INVALID_ARG;
@@ -758,6 +758,31 @@ extern "C" gemv_status gemv_int4_run(gemv_plan_t p, const void *Wq, int64_t ldq,
     if (!aligned16(Wq) || !aligned16(X) || !aligned2(S) || !aligned4(Y))
         return GEMV_ERR_MISALIGNED;
     return bbd::launch_int4(p, Wq, ldq, S, lds, X, Y, stream);
+}
+
+extern "C" gemv_status gemv_rmsnorm_run(gemv_plan_t p, const gemv_segment *segs, int nseg,
+                                        const void *H, const void *gamma, float eps,
+                                        void *stream)
+{
+    if (!p || !segs || nseg < 1 || nseg > GEMV_MAX_SEGMENTS || !H || !gamma ||
+        p->prologue != GEMV_PROLOGUE_RMSNORM || !(eps >= 0.f) || !(eps <= 3.4e38f))
+        return GEMV_ERR_INVALID_ARG;
+    int64_t rows = 0;
+    for (int i = 0; i < nseg; ++i) {
+        const gemv_segment &s = segs[i];
+        if (!s.W || !s.Y || s.n < 1 || s.ldw < p->k || s.ldw > INT32_MAX || s.ldw % 8 != 0 ||
+            s.ldw != segs[0].ldw)
+            return GEMV_ERR_INVALID_ARG;
+        rows += s.n;
+    }
+    if (rows != p->n)
+        return GEMV_ERR_INVALID_ARG;
+    if (!aligned16(H) || !aligned16(gamma))
+        return GEMV_ERR_MISALIGNED;
+    for (int i = 0; i < nseg; ++i)
+        if (!aligned16(segs[i].W) || !aligned4(segs[i].Y))
+            return GEMV_ERR_MISALIGNED;
+    return bbd::launch_rmsnorm(p, segs, nseg, H, gamma, eps, stream);
 }
 
 extern "C" gemv_status gemv_fused_run(gemv_plan_t p, const gemv_segment *segs, int nseg,

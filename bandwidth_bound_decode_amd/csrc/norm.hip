@@ -1,0 +1,179 @@
+// norm.hip - batch-1 GEMV with the RMSNorm of its input fused in front.
+//
+// At decode batch 1 a normalisation moves trivial bytes and costs its launch (GPU performance
+// chains page, "Fused RMSNorm traffic"); the projections that consume the normalised vector
+// (QKV, gate_up) can compute it themselves. Operation: y = rms_inv * W . (gamma * h) with
+// rms_inv = 1 / sqrt(mean(h^2) + eps) and no rounding between the norm and the GEMV.
+//
+// A workgroup of WAVES waves owns WAVES consecutive rows (one per wave) and first builds the
+// normalised input's numerator u = gamma * h in LDS. u is exact in fp32 (two 8-bit
+// significands) but not a bf16 value, so it is stored as the exact sum of two bf16 values,
+// u = hi + lo (hi the bf16 rounding of u, lo = u - hi, which fits in 8 significant bits);
+// the main loop then multiplies each 16-byte weight vector by both halves with
+// v_dot2c_f32_bf16 into two accumulator chains (all products exact), added once per lane
+// at the end. The workgroup also sums h^2 (dot2 of h with itself in per-thread chains, the
+// DPP tree per wave, the waves in order) and takes
+// rms_inv = 1 / sqrt(sum / K + eps) with IEEE fp32 operations; every workgroup does the
+// same arithmetic on the same data, so every row sees the same rms_inv. The row's dot
+// product is then scaled by it once.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "device.h"
+#include "plan.h"
+
+namespace {
+
+using namespace bbd;
+
+struct NormArgs {
+    const uint16_t *h;
+    const uint16_t *gamma;
+    int k;                      // a multiple of 8
+    int ldw;                    // shared by every segment
+    float eps;
+    int nseg;
+    int rows;                   // total rows over the segments
+    int row0[GEMV_MAX_SEGMENTS];   // first global row of each segment (INT_MAX when unused)
+    const uint16_t *w[GEMV_MAX_SEGMENTS];
+    float *y[GEMV_MAX_SEGMENTS];
+};
+
+// bf16 bits of the round-to-nearest-even of a finite float.
+__device__ __forceinline__ unsigned bf16_rne(float f)
+{
+    const unsigned b = __float_as_uint(f);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Elements 2i, 2i+1 of a packed bf16 vector as floats.
+__device__ __forceinline__ float lo_half(unsigned d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float hi_half(unsigned d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+template <int U>
+__global__ void __launch_bounds__(512) gemv_rmsnorm(NormArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int vecs = a.k / kVecElems;
+    u32x4 *uhi = reinterpret_cast<u32x4 *>(lds);
+    u32x4 *ulo = uhi + vecs;
+    float *partials = reinterpret_cast<float *>(ulo + vecs);   // one per wave
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int waves = (int)(blockDim.x >> 6);
+
+    // u = gamma * h as hi + lo in LDS, and this thread's share of sum h^2.
+    float sq = 0.f;
+    for (int v = (int)threadIdx.x; v < vecs; v += (int)blockDim.x) {
+        const u32x4 hv = load_cached(a.h + kVecElems * v);
+        const u32x4 gv = load_cached(a.gamma + kVecElems * v);
+        const unsigned hd[4] = {hv.x, hv.y, hv.z, hv.w};
+        const unsigned gd[4] = {gv.x, gv.y, gv.z, gv.w};
+        unsigned hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float h0 = lo_half(hd[i]), h1 = hi_half(hd[i]);
+            const float u0 = h0 * lo_half(gd[i]), u1 = h1 * hi_half(gd[i]);   // exact
+            sq = dot2(hd[i], hd[i], sq);
+            const unsigned b0 = bf16_rne(u0), b1 = bf16_rne(u1);
+            const unsigned r0 = bf16_rne(u0 - __uint_as_float(b0 << 16));     // exact
+            const unsigned r1 = bf16_rne(u1 - __uint_as_float(b1 << 16));
+            hi[i] = b0 | (b1 << 16);
+            lo[i] = r0 | (r1 << 16);
+        }
+        uhi[v] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        ulo[v] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    const float wsq = lane63(wave_sum(sq));
+    if (lane == 0)
+        partials[wave] = wsq;
+    __syncthreads();
+    float total = partials[0];
+    for (int i = 1; i < waves; ++i)
+        total += partials[i];
+    const float rms_inv = 1.0f / sqrtf(total / (float)a.k + a.eps);
+
+    // This wave's row: segment j = d1 + d2 + d3 (segments are in row order).
+    const int row = blockIdx.x * waves + wave;
+    const int rr = min(row, a.rows - 1);
+    const int d1 = rr >= a.row0[1], d2 = rr >= a.row0[2], d3 = rr >= a.row0[3];
+    const int j = d1 + d2 + d3;
+    const uint16_t *wbase = j == 0 ? a.w[0] : j == 1 ? a.w[1] : j == 2 ? a.w[2] : a.w[3];
+    float *ybase = j == 0 ? a.y[0] : j == 1 ? a.y[1] : j == 2 ? a.y[2] : a.y[3];
+    const int r0 = j == 0 ? a.row0[0] : j == 1 ? a.row0[1] : j == 2 ? a.row0[2] : a.row0[3];
+    const uint16_t *wr = wbase + (int64_t)(rr - r0) * a.ldw;
+
+    // The products with hi and with lo go to separate chains, added once per lane at the end.
+    float acc_hi = 0.f, acc_lo = 0.f;
+    for (int s0 = 0; s0 < vecs; s0 += kWaveLanes * U) {
+        u32x4 wv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            wv[u] = load_stream(wr + kVecElems * min(s0 + lane + kWaveLanes * u, vecs - 1));
+        __builtin_amdgcn_sched_barrier(0);   // the burst's loads before the first use
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = s0 + lane + kWaveLanes * u;
+            const int vc = min(v, vecs - 1);
+            const float nh = dot8(wv[u], uhi[vc], acc_hi);
+            const float nl = dot8(wv[u], ulo[vc], acc_lo);
+            acc_hi = v < vecs ? nh : acc_hi;
+            acc_lo = v < vecs ? nl : acc_lo;
+        }
+    }
+    const float sum = lane63(wave_sum(acc_hi + acc_lo));
+    if (lane == 0 && row < a.rows)
+        ybase[row - r0] = rms_inv * sum;
+}
+
+const void *find_rmsnorm(int u)
+{
+    switch (u) {
+    case 1: return reinterpret_cast<const void *>(&gemv_rmsnorm<1>);
+    case 2: return reinterpret_cast<const void *>(&gemv_rmsnorm<2>);
+    case 4: return reinterpret_cast<const void *>(&gemv_rmsnorm<4>);
+    case 8: return reinterpret_cast<const void *>(&gemv_rmsnorm<8>);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+namespace bbd {
+
+gemv_status launch_rmsnorm(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *H,
+                           const void *gamma, float eps, void *stream)
+{
+    const void *fn = find_rmsnorm(p->unroll);
+    if (!fn)
+        return GEMV_ERR_INVALID_ARG;
+    NormArgs a;
+    a.h = static_cast<const uint16_t *>(H);
+    a.gamma = static_cast<const uint16_t *>(gamma);
+    a.k = (int)p->k;
+    a.ldw = (int)segs[0].ldw;
+    a.eps = eps;
+    a.nseg = nseg;
+    a.rows = (int)p->n;
+    int64_t row0 = 0;
+    for (int i = 0; i < GEMV_MAX_SEGMENTS; ++i) {
+        if (i < nseg) {
+            a.row0[i] = (int)row0;
+            a.w[i] = static_cast<const uint16_t *>(segs[i].W);
+            a.y[i] = segs[i].Y;
+            row0 += segs[i].n;
+        } else {
+            a.row0[i] = INT32_MAX;   // never selected
+            a.w[i] = a.w[0];
+            a.y[i] = a.y[0];
+        }
+    }
+    void *args[] = {&a};
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p->grid_x), dim3((unsigned)p->block_threads),
+                                   args, (size_t)p->lds_bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMV_OK : record_hip_error((int)e, GEMV_ERR_DEVICE);
+}
+
+}  // namespace bbd

@@ -229,6 +229,64 @@ gemv_status plan_int4(gemv_plan_t *out, int64_t n, int64_t k, int m,
     return GEMV_OK;
 }
 
+// RMSNorm prologue, batch 1, unsplit, one row per wave. A product W * hi (or W * lo)
+// passes through its lane's chain (four dot2 per vector, +1 inside the first), the one
+// addition of the two chains, the 6 wave levels and the final scaling; rms_inv carries
+// half the relative error of sum h^2 (per-thread dot2 chains of four per vector, +1, the
+// 6 wave levels and waves - 1 adds) plus the division, square root and reciprocal. The
+// bound adds both (with the final product) as roundings.
+int rmsnorm_depth_for(int64_t k, int waves)
+{
+    const int64_t vecs = ceil_div(k, kVecElems);
+    const int64_t dot = 4 * ceil_div(vecs, kWaveLanes) + 1 + 1 + 6;
+    const int64_t sq = 4 * ceil_div(vecs, (int64_t)kWaveLanes * waves) + 1 + 6 + (waves - 1);
+    return (int)(dot + ceil_div(sq, 2) + 4);
+}
+
+gemv_status plan_rmsnorm(gemv_plan_t *out, int64_t n, int64_t k, int m,
+                         const gemv_device_desc *dev, const gemv_plan_opts &o)
+{
+    if (m != 1 || k % kVecElems != 0 || k > kNormMaxK || o.splits > 1 || o.mfma > 0 ||
+        o.waves_per_cu != 0 || o.rows_per_wave > 1)
+        return GEMV_ERR_INVALID_ARG;
+    const int64_t vecs = k / kVecElems;
+    const int64_t steps = ceil_div(vecs, kWaveLanes);
+    int u = o.unroll ? o.unroll : (steps >= 4 ? 4 : steps >= 2 ? 2 : 1);
+    int waves = o.waves_per_block ? o.waves_per_block : 8;
+    if (!(u == 1 || u == 2 || u == 4 || u == 8) || !valid_waves(waves))
+        return GEMV_ERR_INVALID_ARG;
+    const int depth = rmsnorm_depth_for(k, waves);
+    if (depth > kMaxDepth)
+        return GEMV_ERR_INVALID_ARG;
+    gemv_plan_s *p = new (std::nothrow) gemv_plan_s;
+    if (!p)
+        return GEMV_ERR_INVALID_ARG;
+    memset(p, 0, sizeof *p);
+    p->n = n;
+    p->k = k;
+    p->m = 1;
+    p->device = -1;
+    p->dev = *dev;
+    p->splits = 1;
+    p->rows_per_wave = 1;
+    p->waves_per_block = waves;
+    p->unroll = u;
+    p->slice = k;
+    p->grid_x = (int)ceil_div(n, waves);
+    p->grid_y = 1;
+    p->block_threads = kWaveLanes * waves;
+    p->depth_bound = depth;
+    p->prologue = GEMV_PROLOGUE_RMSNORM;
+    p->lds_bytes = (int)(32 * vecs + 4 * waves);
+    int64_t per_cu = ceil_div((int64_t)p->grid_x * waves, dev->compute_units);
+    if (per_cu > kMaxWavesPerCU)
+        per_cu = kMaxWavesPerCU;
+    p->bif_per_cu = (double)per_cu * u * kWaveLanes * 16.0;
+    p->bif_needed = gemv_bytes_in_flight(dev->hbm_bytes_per_s, dev->latency_s) / dev->compute_units;
+    *out = p;
+    return GEMV_OK;
+}
+
 }  // namespace
 
 extern "C" double gemv_bytes_in_flight(double bytes_per_s, double latency_s)
@@ -249,11 +307,15 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     // Row indices and grid sizes are held in 32 bits on the device.
     if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30)
         return GEMV_ERR_INVALID_ARG;
-    gemv_plan_opts o = {0, 0, 0, 0, 0, 0, 0};
+    gemv_plan_opts o = {0, 0, 0, 0, 0, 0, 0, 0};
     if (opts)
         o = *opts;
     if (o.splits < 0 || o.rows_per_wave < 0 || o.waves_per_block < 0 || o.unroll < 0 ||
         o.waves_per_cu < -1 || o.waves_per_cu > kMaxWavesPerCU || o.mfma < -1 || o.mfma > 1)
+        return GEMV_ERR_INVALID_ARG;
+    if (o.prologue == GEMV_PROLOGUE_RMSNORM && o.weights == GEMV_WEIGHTS_BF16)
+        return plan_rmsnorm(out, n, k, m, dev, o);
+    if (o.prologue != 0)
         return GEMV_ERR_INVALID_ARG;
     if (o.weights == GEMV_WEIGHTS_INT4)
         return plan_int4(out, n, k, m, dev, o);
@@ -437,6 +499,7 @@ extern "C" gemv_status gemv_plan_query(gemv_plan_t p, gemv_plan_info *info)
     info->mfma_grid_x = p->mfma_grid_x;
     info->mfma_depth_bound = p->mfma_depth;
     info->weights = p->weights;
+    info->prologue = p->prologue;
     return GEMV_OK;
 }
 

@@ -86,6 +86,11 @@ gemv_status launch_batch(gemv_plan_t p, const gemv_segment *segs, int nseg, cons
 gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
                         int64_t ldx, void *ws, void *stream, bool *done);
 
+// RMSNorm-prologue launch (norm.hip) of a validated call; the plan's unroll picks the kernel.
+gemv_status launch_rmsnorm(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *H,
+                           const void *gamma, float eps, void *stream);
+constexpr int64_t kNormMaxK = 16368;   // 4K + 64 bytes of LDS (hi and lo halves, wave sums)
+
 // INT4-weight launch (int4.hip) of a validated call; the plan's unroll, rows per wave and
 // LDS size pick the kernel.
 gemv_status launch_int4(gemv_plan_t p, const void *Wq, int64_t ldq, const void *S, int64_t lds,
@@ -120,4 +125,5 @@ struct gemv_plan_s {
     int mfma_grid_x;
     int mfma_depth;
     int weights;                // GEMV_WEIGHTS_BF16 or GEMV_WEIGHTS_INT4
+    int prologue;               // 0 or GEMV_PROLOGUE_RMSNORM
 };

@@ -88,7 +88,11 @@ typedef struct {
     int waves_per_cu;
     int mfma;
     int weights;        /* GEMV_WEIGHTS_BF16 (0) or GEMV_WEIGHTS_INT4; see gemv_int4_run */
+    int prologue;       /* 0, or GEMV_PROLOGUE_RMSNORM; see gemv_rmsnorm_run */
 } gemv_plan_opts;
+
+/* Input prologues a plan can be made for. */
+#define GEMV_PROLOGUE_RMSNORM 1
 
 /* Weight formats a plan can be made for. */
 #define GEMV_WEIGHTS_BF16 0
@@ -130,6 +134,7 @@ typedef struct {
     int mfma_grid_x;        /* 32-row blocks: ceil(N / 32); 8 waves per workgroup */
     int mfma_depth_bound;   /* h for that kernel, counting 32 roundings per MFMA */
     int weights;            /* the plan's weight format */
+    int prologue;           /* the plan's input prologue (0: none) */
 } gemv_plan_info;
 
 /*
@@ -235,6 +240,26 @@ gemv_status gemv_fused_run(gemv_plan_t p, const gemv_segment *segs, int nseg,
  */
 gemv_status gemv_int4_run(gemv_plan_t p, const void *Wq, int64_t ldq, const void *S,
                           int64_t lds, const void *X, float *Y, void *stream);
+
+/*
+ * Batch-1 GEMV of the RMS-normalised input (GPU performance chains page, "Fused RMSNorm
+ * traffic": at decode a normalisation's bytes are trivial and its launch is the cost, so
+ * the projections that consume it compute it themselves):
+ *   rms_inv = 1 / sqrt( sum_k H[k]^2 / K + eps ),
+ *   Y_i[n]  = rms_inv * sum_k W_i[n][k] * (gamma[k] * H[k])
+ * for every segment i (one launch; QKV and gate_up pass their matrices as segments, as in
+ * gemv_fused_run), with no rounding between the norm and the GEMV; within the gemv_run
+ * tolerance, with s_abs = rms_inv * sum_k |W[n][k] gamma[k] H[k]|.
+ * The plan must come from gemv_plan / gemv_plan_for with opts.prologue =
+ * GEMV_PROLOGUE_RMSNORM, m = 1 and k a multiple of 8 up to 16368 (the numerator gamma*H is
+ * staged in LDS); it never splits K. H and gamma are bf16 [k], 16-byte aligned; every W_i
+ * is 16-byte aligned with one shared ldw, a multiple of 8 (else GEMV_ERR_MISALIGNED /
+ * GEMV_ERR_INVALID_ARG); each Y_i is fp32 [n_i] (the segments' ldy is not used); eps >= 0
+ * and finite. No workspace; no allocation or host synchronisation (capture-safe).
+ * gemv_run and gemv_fused_run reject these plans, and this call rejects any other plan.
+ */
+gemv_status gemv_rmsnorm_run(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *H,
+                             const void *gamma, float eps, void *stream);
 
 /*
  * Graph capture of a GEMV sequence, so a whole decode step crosses the host-device boundary
