@@ -5,8 +5,8 @@
 // (QKV, gate_up) can compute it themselves. Operation: y = rms_inv * W . (gamma * h) with
 // rms_inv = 1 / sqrt(mean(h^2) + eps) and no rounding between the norm and the GEMV.
 //
-// A workgroup of WAVES waves owns WAVES consecutive rows (one per wave) and first builds the
-// normalised input's numerator u = gamma * h in LDS. u is exact in fp32 (two 8-bit
+// A workgroup of WAVES waves takes blocks of WAVES consecutive rows (one per wave) and first
+// builds the normalised input's numerator u = gamma * h in LDS. u is exact in fp32 (two 8-bit
 // significands) but not a bf16 value, so it is stored as the exact sum of two bf16 values,
 // u = hi + lo (hi the bf16 rounding of u, lo = u - hi, which fits in 8 significant bits);
 // the main loop then multiplies each 16-byte weight vector by both halves with
@@ -52,6 +52,42 @@ __device__ __forceinline__ unsigned bf16_rne(float f)
 __device__ __forceinline__ float lo_half(unsigned d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float hi_half(unsigned d) { return __uint_as_float(d & 0xFFFF0000u); }
 
+struct NormRow {
+    const uint16_t *w;
+    float *y;
+};
+
+// The weight row of global row `row` (clamped onto the last row) and its output slot.
+// Segments are in row order, so segment j = d1 + d2 + d3 with d_i = (row >= row0[i]); the
+// pointers are segment 0's plus the sum of d_i times the step to segment i (arithmetic, not
+// a select chain, which would move the arguments to scratch).
+__device__ __forceinline__ NormRow norm_row(const NormArgs &a, int row)
+{
+    const int rr = min(row, a.rows - 1);
+    const int64_t d1 = rr >= a.row0[1], d2 = rr >= a.row0[2], d3 = rr >= a.row0[3];
+    const int64_t w0 = (int64_t)a.w[0], y0 = (int64_t)a.y[0];
+    const int64_t dw = d1 * ((int64_t)a.w[1] - w0) + d2 * ((int64_t)a.w[2] - (int64_t)a.w[1]) +
+                       d3 * ((int64_t)a.w[3] - (int64_t)a.w[2]);
+    const int64_t dy = d1 * ((int64_t)a.y[1] - y0) + d2 * ((int64_t)a.y[2] - (int64_t)a.y[1]) +
+                       d3 * ((int64_t)a.y[3] - (int64_t)a.y[2]);
+    const int local = rr - (int)(d1 * (a.row0[1] - a.row0[0]) + d2 * (a.row0[2] - a.row0[1]) +
+                                 d3 * (a.row0[3] - a.row0[2]));
+    return {a.w[0] + dw / (int64_t)sizeof(uint16_t) + (int64_t)local * a.ldw,
+            a.y[0] + dy / (int64_t)sizeof(float) + local};
+}
+
+template <int U>
+__device__ __forceinline__ void norm_burst(const uint16_t *wr, int s0, int vecs, int lane,
+                                           u32x4 (&wv)[U])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        wv[u] = load_stream(wr + kVecElems * min(s0 + lane + kWaveLanes * u, vecs - 1));
+}
+
+// Workgroups take row blocks (one row per wave) blockIdx.x, blockIdx.x + gridDim.x, ...,
+// so the staging is paid once per workgroup; the first burst of the first row is issued
+// before the staging, so its latency and the staging's overlap.
 template <int U>
 __global__ void __launch_bounds__(512) gemv_rmsnorm(NormArgs a)
 {
@@ -63,6 +99,12 @@ __global__ void __launch_bounds__(512) gemv_rmsnorm(NormArgs a)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int waves = (int)(blockDim.x >> 6);
+    const int blocks = (a.rows + waves - 1) / waves;
+
+    int blk = blockIdx.x;
+    NormRow nr = norm_row(a, blk * waves + wave);
+    u32x4 wv[U];
+    norm_burst<U>(nr.w, 0, vecs, lane, wv);
 
     // u = gamma * h as hi + lo in LDS, and this thread's share of sum h^2.
     float sq = 0.f;
@@ -74,11 +116,11 @@ __global__ void __launch_bounds__(512) gemv_rmsnorm(NormArgs a)
         unsigned hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float h0 = lo_half(hd[i]), h1 = hi_half(hd[i]);
-            const float u0 = h0 * lo_half(gd[i]), u1 = h1 * hi_half(gd[i]);   // exact
+            const float u0 = lo_half(hd[i]) * lo_half(gd[i]);   // exact
+            const float u1 = hi_half(hd[i]) * hi_half(gd[i]);
             sq = dot2(hd[i], hd[i], sq);
             const unsigned b0 = bf16_rne(u0), b1 = bf16_rne(u1);
-            const unsigned r0 = bf16_rne(u0 - __uint_as_float(b0 << 16));     // exact
+            const unsigned r0 = bf16_rne(u0 - __uint_as_float(b0 << 16));   // exact
             const unsigned r1 = bf16_rne(u1 - __uint_as_float(b1 << 16));
             hi[i] = b0 | (b1 << 16);
             lo[i] = r0 | (r1 << 16);
@@ -95,37 +137,32 @@ __global__ void __launch_bounds__(512) gemv_rmsnorm(NormArgs a)
         total += partials[i];
     const float rms_inv = 1.0f / sqrtf(total / (float)a.k + a.eps);
 
-    // This wave's row: segment j = d1 + d2 + d3 (segments are in row order).
-    const int row = blockIdx.x * waves + wave;
-    const int rr = min(row, a.rows - 1);
-    const int d1 = rr >= a.row0[1], d2 = rr >= a.row0[2], d3 = rr >= a.row0[3];
-    const int j = d1 + d2 + d3;
-    const uint16_t *wbase = j == 0 ? a.w[0] : j == 1 ? a.w[1] : j == 2 ? a.w[2] : a.w[3];
-    float *ybase = j == 0 ? a.y[0] : j == 1 ? a.y[1] : j == 2 ? a.y[2] : a.y[3];
-    const int r0 = j == 0 ? a.row0[0] : j == 1 ? a.row0[1] : j == 2 ? a.row0[2] : a.row0[3];
-    const uint16_t *wr = wbase + (int64_t)(rr - r0) * a.ldw;
-
-    // The products with hi and with lo go to separate chains, added once per lane at the end.
-    float acc_hi = 0.f, acc_lo = 0.f;
-    for (int s0 = 0; s0 < vecs; s0 += kWaveLanes * U) {
-        u32x4 wv[U];
+    for (;;) {
+        // The products with hi and with lo go to separate chains, added once per lane.
+        float acc_hi = 0.f, acc_lo = 0.f;
+        for (int s0 = 0; s0 < vecs; s0 += kWaveLanes * U) {
+            if (s0 > 0)
+                norm_burst<U>(nr.w, s0, vecs, lane, wv);
+            __builtin_amdgcn_sched_barrier(0);   // the burst's loads before the first use
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            wv[u] = load_stream(wr + kVecElems * min(s0 + lane + kWaveLanes * u, vecs - 1));
-        __builtin_amdgcn_sched_barrier(0);   // the burst's loads before the first use
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = s0 + lane + kWaveLanes * u;
-            const int vc = min(v, vecs - 1);
-            const float nh = dot8(wv[u], uhi[vc], acc_hi);
-            const float nl = dot8(wv[u], ulo[vc], acc_lo);
-            acc_hi = v < vecs ? nh : acc_hi;
-            acc_lo = v < vecs ? nl : acc_lo;
+            for (int u = 0; u < U; ++u) {
+                const int v = s0 + lane + kWaveLanes * u;
+                const int vc = min(v, vecs - 1);
+                const float nh = dot8(wv[u], uhi[vc], acc_hi);
+                const float nl = dot8(wv[u], ulo[vc], acc_lo);
+                acc_hi = v < vecs ? nh : acc_hi;
+                acc_lo = v < vecs ? nl : acc_lo;
+            }
         }
+        const float sum = lane63(wave_sum(acc_hi + acc_lo));
+        if (lane == 0 && blk * waves + wave < a.rows)
+            *nr.y = rms_inv * sum;
+        blk += gridDim.x;
+        if (blk >= blocks)
+            break;
+        nr = norm_row(a, blk * waves + wave);
+        norm_burst<U>(nr.w, 0, vecs, lane, wv);
     }
-    const float sum = lane63(wave_sum(acc_hi + acc_lo));
-    if (lane == 0 && row < a.rows)
-        ybase[row - r0] = rms_inv * sum;
 }
 
 const void *find_rmsnorm(int u)

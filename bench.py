@@ -231,6 +231,65 @@ def bench_int4(torch, bbd, workloads, name, n, k, steps, warmup):
     return res
 
 
+def bench_rmsnorm(torch, bbd, workloads, name, segments, k, steps):
+    """A projection with its RMSNorm prologue fused (gemv_rmsnorm_run) against the same
+    projection without it (gemv_fused_run on an already normalised x), both rotated and back
+    to back in one graph, and against the norm as a separate launch (torch's rms_norm),
+    timed back to back eagerly."""
+    n = sum(segments)
+    gen = workloads.generator(4000 + n % 997, "cuda")
+    w = workloads.bf16_normal((n, k), workloads.SIGMA_W, gen, "cuda")
+    h = workloads.bf16_normal((k,), workloads.SIGMA_X, gen, "cuda")
+    gain = (1.0 + 0.1 * torch.randn((k,), generator=gen, device="cuda")).to(torch.bfloat16)
+    arena = rotation_arena(torch, w)
+    copies = arena.shape[0]
+    bounds = [0]
+    for seg in segments:
+        bounds.append(bounds[-1] + seg)
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    ys = [y[0, a:b] for a, b in zip(bounds[:-1], bounds[1:])]
+    ys2 = [y[:, a:b] for a, b in zip(bounds[:-1], bounds[1:])]
+    norm_plan = bbd.Plan(n, k, 1, prologue="rmsnorm")
+    plain_plan = bbd.Plan(n, k, 1)
+    x = h[None, :].clone()
+
+    def fused(i, stream=None):
+        wi = arena[i % copies]
+        bbd.rmsnorm_run(norm_plan, [(wi[a:b], yy) for (a, b), yy in
+                                    zip(zip(bounds[:-1], bounds[1:]), ys)], h, gain, 1e-5,
+                        stream)
+
+    def plain(i, stream=None):
+        wi = arena[i % copies]
+        if len(segments) == 1:
+            bbd.run(plain_plan, wi, x, y, None, stream)
+        else:
+            bbd.fused_run(plain_plan, [(wi[a:b], yy) for (a, b), yy in
+                                       zip(zip(bounds[:-1], bounds[1:]), ys2)], x, None, stream)
+    side = torch.cuda.Stream()
+    t_fused = time_graph(torch, lambda i: fused(i, side), steps, side) / steps
+    t_plain = time_graph(torch, lambda i: plain(i, side), steps, side) / steps
+    # the norm as its own launch, eagerly back to back (torch's kernel; not on the GEMV path)
+    for _ in range(10):
+        torch.nn.functional.rms_norm(h.float(), (k,), gain.float(), 1e-5)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        torch.nn.functional.rms_norm(h.float(), (k,), gain.float(), 1e-5)
+    b.record()
+    torch.cuda.synchronize()
+    t_norm = a.elapsed_time(b) / 1e3 / steps
+    del arena
+    return {"name": name, "shape": f"{n}x{k}", "segments": list(segments),
+            "fused_norm_gemv_us": t_fused * 1e6, "gemv_without_norm_us": t_plain * 1e6,
+            "prologue_cost_us": (t_fused - t_plain) * 1e6,
+            "separate_torch_rms_norm_eager_us": t_norm * 1e6,
+            "plan": {key: norm_plan.info[key] for key in ("unroll", "waves_per_block",
+                                                          "grid_x", "lds_bytes")}}
+
+
 def bench_decode_step_int4(torch, bbd, workloads, replays):
     """The same 129-GEMV decode step with INT4 weights: every projection (QKV and gate_up as
     one row-concatenated matrix each) through gemv_int4_run, captured in one graph, in stream
@@ -454,6 +513,16 @@ def main(argv=None):
                     r[k] = round(r[k], 3)
             log(f"{name}: {r['us_median']:.2f} us, {r['TBps_median']:.3f} TB/s")
             out.setdefault("shapes", []).append(r)
+        # the RMSNorm prologue fused into the projections that consume the normalised x
+        for name, segs in (("rmsnorm_qkv", (4096, 1024, 1024)), ("rmsnorm_gate_up", (14336, 14336))):
+            r = bench_rmsnorm(torch, bbd, workloads, name, segs, 4096, args.shape_steps)
+            for key in list(r):
+                if isinstance(r[key], float):
+                    r[key] = round(r[key], 3)
+            log(f"{name}: fused {r['fused_norm_gemv_us']:.2f} us, without the norm "
+                f"{r['gemv_without_norm_us']:.2f} us, a separate norm launch "
+                f"{r['separate_torch_rms_norm_eager_us']:.2f} us")
+            out.setdefault("rmsnorm_prologue", []).append(r)
         # INT4 weights at the same projection shapes (batch 1)
         for name, n, k in (("int4_down", 4096, 14336), ("int4_k_proj", 1024, 4096),
                            ("int4_o_proj", 4096, 4096), ("int4_qkv", 6144, 4096),

@@ -283,8 +283,10 @@ def test_rmsnorm_plans():
     workgroup sharing the staged numerator, no split or workspace."""
     i = plan(6144, 4096, prologue="rmsnorm").info
     assert i["prologue"] == 1 and i["weights"] == 0 and i["mfma"] == 0 and i["splits"] == 1
-    assert (i["rows_per_wave"], i["waves_per_block"], i["unroll"]) == (1, 8, 4)
-    assert (i["grid_x"], i["block_threads"], i["lds_bytes"]) == (768, 512, 32 * 512 + 4 * 8)
+    assert (i["rows_per_wave"], i["waves_per_block"], i["unroll"]) == (1, 8, 8)
+    assert (i["grid_x"], i["block_threads"], i["lds_bytes"]) == (512, 512, 32 * 512 + 4 * 8)
+    assert plan(1024, 4096, prologue="rmsnorm").info["grid_x"] == 128   # one row block each
+    assert plan(28672, 4096, prologue="rmsnorm").info["grid_x"] == 1024  # 14 blocks per CU
     # 4 dot2 per vector x 8 vectors + 8, half of (4 + 1 + 6 + 7) rounded up, 4 for the scale
     assert i["depth_bound"] == 40 + 9 + 4
     assert plan(6144, 4096, prologue="rmsnorm").workspace_size == 0
@@ -292,10 +294,13 @@ def test_rmsnorm_plans():
     assert plan(4096, 16368, prologue="rmsnorm").info["depth_bound"] <= 160
     assert plan(6144, 4096).info["prologue"] == 0
     for bad in (dict(k=100), dict(k=16376), dict(m=2), dict(splits=2), dict(mfma=1),
-                dict(waves_per_cu=8), dict(rows_per_wave=2), dict(unroll=3),
-                dict(waves_per_block=3), dict(weights="int4")):
+                dict(rows_per_wave=2), dict(unroll=3), dict(waves_per_block=3),
+                dict(weights="int4")):
         args = dict(n=64, k=4096, m=1)
         args.update({k: v for k, v in bad.items() if k in args})
         opts = {k: v for k, v in bad.items() if k not in args}
         with pytest.raises(bbd.GemvError):
             plan(args["n"], args["k"], args["m"], prologue="rmsnorm", **opts)
+    # the resident-wave option sizes the looping grid
+    assert plan(28672, 4096, prologue="rmsnorm", waves_per_cu=32).info["grid_x"] == 1024
+    assert plan(28672, 4096, prologue="rmsnorm", waves_per_cu=-1).info["grid_x"] == 3584
