@@ -34,9 +34,8 @@ struct NormArgs {
     int k;                      // a multiple of 8
     int ldw;                    // shared by every segment
     float eps;
-    int nseg;
     int rows;                   // total rows over the segments
-    int row0[GEMV_MAX_SEGMENTS];   // first global row of each segment (INT_MAX when unused)
+    int row0[GEMV_MAX_SEGMENTS];   // first global row of each segment (INT32_MAX when unused)
     const uint16_t *w[GEMV_MAX_SEGMENTS];
     float *y[GEMV_MAX_SEGMENTS];
 };
@@ -192,7 +191,6 @@ gemv_status launch_rmsnorm(gemv_plan_t p, const gemv_segment *segs, int nseg, co
     a.k = (int)p->k;
     a.ldw = (int)segs[0].ldw;
     a.eps = eps;
-    a.nseg = nseg;
     a.rows = (int)p->n;
     int64_t row0 = 0;
     for (int i = 0; i < GEMV_MAX_SEGMENTS; ++i) {

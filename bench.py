@@ -354,8 +354,48 @@ def bench_decode_step(torch, bbd, workloads, replays, warmup):
         _, chain_per = time_launches(torch, lambda i: cg.launch(stream), replays, warmup,
                                      stream)
     chain.check()
+    # The same step with the RMSNorm prologue fused into every call that consumes a
+    # normalised vector in a Llama layer (QKV, gate_up) and into lm_head (the final norm):
+    # each such call reads its x as the residual stream h plus a gain, eps 1e-5.
+    gen = workloads.generator(5000, "cuda")
+    norm_plans, norm_gain, nb_norm = {}, [], nb
+    for c in calls:
+        name_ok = len(c.weights) > 1 or c.weights[0].shape[0] == workloads.VOCAB
+        if name_ok:
+            key = (c.n, c.x.shape[-1])
+            if key not in norm_plans:
+                norm_plans[key] = bbd.Plan(c.n, c.x.shape[-1], 1, prologue="rmsnorm")
+            norm_gain.append((1.0 + 0.1 * torch.randn((c.x.shape[-1],), generator=gen,
+                                                       device="cuda")).to(torch.bfloat16))
+            nb_norm += 2 * c.x.shape[-1]
+        else:
+            norm_gain.append(None)
+
+    def run_with_norms(stream):
+        for c, g in zip(calls, norm_gain):
+            if g is None:
+                if len(c.weights) == 1:
+                    bbd.run(c.plan, c.weights[0], c.x, c.ys[0], seq.workspace, stream)
+                else:
+                    bbd.fused_run(c.plan, list(zip(c.weights, c.ys)), c.x, seq.workspace,
+                                  stream)
+            else:
+                bbd.rmsnorm_run(norm_plans[(c.n, c.x.shape[-1])],
+                                [(w, y[0]) for w, y in zip(c.weights, c.ys)], c.x[0], g,
+                                1e-5, stream)
+    with torch.cuda.stream(stream):
+        ng = bbd.Graph(stream)
+        with ng:
+            run_with_norms(stream)
+        _, norm_per = time_launches(torch, lambda i: ng.launch(stream), replays, warmup,
+                                    stream)
+    ng.destroy()
     out = {"gemvs": len(calls), "alg_bytes": nb, "weight_bytes": seq.weight_bytes,
            "replays": replays}
+    t = statistics.median(norm_per)
+    out["graph_with_rmsnorm_prologues_ms_median"] = t * 1e3
+    out["graph_with_rmsnorm_prologues_mbu"] = mbu(nb_norm, t, PEAK_HBM)
+    out["rmsnorm_prologue_calls"] = sum(g is not None for g in norm_gain)
     for name, per in (("eager", eager_per), ("graph", graph_per), ("chain_graph", chain_per)):
         t = statistics.median(per)
         out[f"{name}_ms_median"] = t * 1e3
@@ -544,7 +584,8 @@ def main(argv=None):
         log(f"decode step: chain in a graph {d['chain_graph_ms_median']:.3f} ms "
             f"(MBU {d['chain_graph_mbu']:.3f}); graph of 129 launches "
             f"{d['graph_ms_median']:.3f} ms (MBU {d['graph_mbu']:.3f}); eager "
-            f"{d['eager_ms_median']:.3f} ms")
+            f"{d['eager_ms_median']:.3f} ms; graph with {d['rmsnorm_prologue_calls']} fused "
+            f"RMSNorm prologues {d['graph_with_rmsnorm_prologues_ms_median']:.3f} ms")
         torch.cuda.empty_cache()
         d4 = bench_decode_step_int4(torch, bbd, workloads, args.decode_replays)
         for k in list(d4):
