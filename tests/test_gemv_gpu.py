@@ -279,3 +279,15 @@ def test_large_x_stride():
         oracle_check(W, X, Y, f"k={k} ldx={ldx} m={m} mfma={p.info['mfma']}")
         del X
         torch.cuda.empty_cache()
+
+
+def test_a_million_rows():
+    """N = 2^20 short rows: a million single-wave workgroups at batch 1, and 32,768 matrix-core
+    blocks at batch 16, checked in full."""
+    n, k = 1 << 20, 64
+    for m in (1, 16):
+        w, x = draw(n, k, m, seed=m)
+        W, X = device_matrix(w), device_matrix(x)
+        Y, p = gemv(W, X)
+        print(m, p.info, flush=True)
+        oracle_check(W, X, Y, f"n=2^20 m={m}")
