@@ -32,6 +32,7 @@
 #include <string.h>
 
 #include <array>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -500,6 +501,165 @@ __global__ void __launch_bounds__(512) gemv_unaligned(ArgsT<MULTI> p)
         combine_if_last<MULTI>(p, M, waves * rows_per_wave);
 }
 
+// Unsplit single-matrix calls whose X fits in LDS take this form of the unaligned path. Rows
+// whose W addresses have the same offset from the 16-byte grid - row r and r + T, where T =
+// 8 / gcd(ldw, 8) - start their vectors at the same element h and so meet the same x
+// windows; a workgroup owns rows of one such class (blockIdx.y), copies the M shifted x rows
+// into LDS once, and its waves then stream W with aligned loads and read the windows from
+// LDS, exactly as the aligned kernels read x. Each lane takes vectors l, l + 64, ... in
+// increasing order and then the head and tail elements, as gemv_unaligned does, so both
+// give bitwise the same result.
+constexpr int kShiftRows = 2;   // rows per wave
+constexpr int kShiftUnroll = 2; // vectors per lane and row per burst
+
+template <int M>
+__global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes)
+{
+    constexpr int R = kShiftRows, U = kShiftUnroll;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    u32x4 *xs = reinterpret_cast<u32x4 *>(lds);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int waves = (int)(blockDim.x >> 6);
+    const int cls = blockIdx.y;
+    const int class_rows = (p.n - cls + classes - 1) / classes;
+    if (class_rows <= 0)   // fewer rows than classes: this workgroup has none (uniform exit)
+        return;
+    const int j0 = (blockIdx.x * waves + wave) * R;
+    const uint16_t *w_cls = p.w0 + (int64_t)cls * p.ldw0;
+    const int h = (int)((8u - (unsigned)(((uintptr_t)w_cls >> 1) & 7u)) & 7u);
+    const int ka = min(h, p.k);
+    const int nvec = ka + 8 <= p.k ? (p.k - ka) >> 3 : 0;
+    const int tail_begin = ka + 8 * nvec;
+    int q[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        q[m] = (int)((((uintptr_t)(p.x + (int64_t)m * p.ldx) >> 1) + (unsigned)h) & 7u);
+
+    const uint16_t *wr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {   // rows past the class re-read its last row, unstored
+        const int j = min(j0 + r, class_rows - 1);
+        wr[r] = p.w0 + (int64_t)(cls + classes * j) * p.ldw0 + ka;
+    }
+    u32x4 wv[U][R];
+    auto burst = [&](int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                wv[u][r] = load_stream(wr[r] + 8 * min(s0 + lane + 64 * u, nvec - 1));
+    };
+    if (nvec > 0)
+        burst(0);   // the first weights are in flight while x is staged
+
+    // Windows inside every row of X (vectors [vlo, vend)) are read without branches, SV per
+    // thread and row of X in flight before any is written; the at most two others element
+    // by element afterwards.
+    constexpr int SV = M <= 4 ? 4 : M <= 8 ? 2 : 1;
+    const int threads = (int)blockDim.x;
+    const int vlo = ka >= 1 ? 0 : 1;
+    const int vhi = p.k - 10 - ka >= 0 ? ((p.k - 10 - ka) >> 3) + 1 : 0;
+    const int vend = min(nvec, vhi);
+    const int tid = (int)threadIdx.x;
+    if (vend > vlo) {
+        for (int v0 = vlo + tid; v0 < vend; v0 += SV * threads) {
+            u32x4 t[SV][M];
+#pragma unroll
+            for (int i = 0; i < SV; ++i) {
+                const int vc = min(v0 + i * threads, vend - 1);
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    t[i][m] = x_window_interior(p.x + (int64_t)m * p.ldx, ka + 8 * vc, q[m]);
+            }
+#pragma unroll
+            for (int i = 0; i < SV; ++i) {
+                const int v = v0 + i * threads;
+                if (v < vend) {
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        xs[m * nvec + v] = t[i][m];
+                }
+            }
+        }
+        // the edge vectors: [0, vlo) and [vend, nvec), at most one each, one per thread
+        const int v = tid < vlo ? tid : vend + (tid - vlo);
+        if (v < nvec) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                xs[m * nvec + v] = x_window(p.x + (int64_t)m * p.ldx, ka + 8 * v, p.k, q[m]);
+        }
+    } else {
+        for (int v = tid; v < nvec; v += threads) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                xs[m * nvec + v] = x_window(p.x + (int64_t)m * p.ldx, ka + 8 * v, p.k, q[m]);
+        }
+    }
+    __syncthreads();
+
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            acc[r][m] = 0.f;
+    for (int s0 = 0; s0 < nvec; s0 += 64 * U) {
+        if (s0 > 0)
+            burst(s0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = s0 + lane + 64 * u;
+            const int vc = min(v, nvec - 1);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const u32x4 xv = xs[m * nvec + vc];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float next = dot8(wv[u][r], xv, acc[r][m]);
+                    acc[r][m] = v < nvec ? next : acc[r][m];
+                }
+            }
+        }
+    }
+    // Lanes 0..7 take the head elements, lanes 8..15 the tail elements.
+    const int kk = lane < 8 ? lane : tail_begin + (lane - 8);
+    const bool take = lane < 8 ? kk < ka : (lane < 16 && kk < p.k);
+    if (take) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float w = bf16_to_f32(wr[r][kk - ka]);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                acc[r][m] = fmaf(w, bf16_to_f32(p.x[(int64_t)m * p.ldx + kk]), acc[r][m]);
+        }
+    }
+    float out = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float sum = lane63(wave_sum(acc[r][m]));
+            if (lane == r * M + m)
+                out = sum;
+        }
+    if (lane < R * M) {
+        const int r = lane / M, m = lane - (lane / M) * M;
+        if (j0 + r < class_rows)
+            p.y0[(int64_t)m * p.ldy0 + cls + classes * (j0 + r)] = out;
+    }
+}
+
+template <size_t... I>
+std::array<const void *, GEMV_MAX_M> unaligned_lds_table(std::index_sequence<I...>)
+{
+    return {reinterpret_cast<const void *>(&gemv_unaligned_lds<(int)I + 1>)...};
+}
+
+const std::array<const void *, GEMV_MAX_M> kUnalignedLds =
+    unaligned_lds_table(std::make_index_sequence<GEMV_MAX_M>{});
+
 // ---------------------------------------------------------------------------- dispatch
 // Kernel handles for hipLaunchKernel; fused instances take ArgsMulti, the others Args.
 template <size_t I, bool SPLIT, bool MULTI>
@@ -548,6 +708,59 @@ const void *find_fast(int m, int r, int u, bool split, bool multi)
 }
 
 gemv_status device_error(hipError_t e) { return record_hip_error((int)e, GEMV_ERR_DEVICE); }
+
+constexpr size_t kShiftMaxLds = 128 * 1024;   // staged x for the class-staged unaligned kernel
+
+// Launch an unsplit single-matrix unaligned call on gemv_unaligned_lds when the M shifted
+// x rows fit in LDS; *done tells whether it did.
+gemv_status launch_unaligned_lds(gemv_plan_t p, const gemv_segment &seg, const void *X,
+                                 int64_t ldx, void *stream, bool *done)
+{
+    *done = false;
+    const size_t bytes = (size_t)p->m * (size_t)(p->k / 8) * sizeof(u32x4);
+    if (p->splits != 1 || bytes == 0 || bytes > kShiftMaxLds)
+        return GEMV_OK;
+    const void *fn = kUnalignedLds[p->m - 1];
+    static std::atomic<bool> allowed[GEMV_MAX_M + 1];
+    if (bytes > 64 * 1024 && !allowed[p->m].load(std::memory_order_acquire)) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)kShiftMaxLds);
+        if (e != hipSuccess)
+            return device_error(e);
+        allowed[p->m].store(true, std::memory_order_release);
+    }
+    *done = true;
+    // Rows r and r + classes start at the same offset from the 16-byte grid.
+    int g = (int)(seg.ldw % 8);
+    int classes = 8;
+    if (g == 0)
+        classes = 1;
+    else if (g % 4 == 0)
+        classes = 2;
+    else if (g % 2 == 0)
+        classes = 4;
+    const int waves = 8;
+    const int64_t class_rows = (p->n + classes - 1) / classes;
+    const int64_t blocks = (class_rows + (int64_t)kShiftRows * waves - 1) / ((int64_t)kShiftRows * waves);
+    Args a;
+    memset(&a, 0, sizeof a);
+    a.w0 = static_cast<const uint16_t *>(seg.W);
+    a.y0 = seg.Y;
+    a.x = static_cast<const uint16_t *>(X);
+    a.ldw0 = (int32_t)seg.ldw;
+    a.ldy0 = (int32_t)seg.ldy;
+    a.ldx = p->m > 1 ? (int32_t)ldx : 0;
+    a.n = (int32_t)p->n;
+    a.k = (int32_t)p->k;
+    a.slice = (int32_t)p->k;
+    a.waves = waves;
+    a.rows = kShiftRows;
+    void *args[] = {&a, &classes};
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks, (unsigned)classes),
+                                   dim3(kWaveLanes * waves), args, bytes,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMV_OK : device_error(e);
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
@@ -609,6 +822,11 @@ gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void
     st = bbd::launch_batch(p, segs, nseg, X, ldx, stream, &done);
     if (done || st != GEMV_OK)
         return st;
+    if (!fast && nseg == 1) {
+        st = launch_unaligned_lds(p, segs[0], X, ldx, stream, &done);
+        if (done || st != GEMV_OK)
+            return st;
+    }
 
     ArgsMulti a;
     memset(&a, 0, sizeof a);
