@@ -501,21 +501,26 @@ __global__ void __launch_bounds__(512) gemv_unaligned(ArgsT<MULTI> p)
         combine_if_last<MULTI>(p, M, waves * rows_per_wave);
 }
 
-// Unsplit single-matrix calls whose X fits in LDS take this form of the unaligned path. Rows
-// whose W addresses have the same offset from the 16-byte grid - row r and r + T, where T =
-// 8 / gcd(ldw, 8) - start their vectors at the same element h and so meet the same x
-// windows; a workgroup owns rows of one such class (blockIdx.y), copies the M shifted x rows
-// into LDS once, and its waves then stream W with aligned loads and read the windows from
-// LDS, exactly as the aligned kernels read x. Each lane takes vectors l, l + 64, ... in
-// increasing order and then the head and tail elements, as gemv_unaligned does, so both
-// give bitwise the same result.
-constexpr int kShiftRows = 2;   // rows per wave
-constexpr int kShiftUnroll = 2; // vectors per lane and row per burst
+// Unsplit single-matrix calls take this form of the unaligned path. Rows whose W addresses
+// have the same offset from the 16-byte grid - row r and r + T, where T = 8 / gcd(ldw, 8) -
+// start their vectors at the same element h and so meet the same x windows; a workgroup owns
+// rows of one such class (blockIdx.y), copies the M shifted x rows into LDS, and its waves
+// then stream W with aligned loads and read the windows from LDS, exactly as the aligned
+// kernels read x. When the M rows do not fit, they are staged `chunk` vectors at a time,
+// with a barrier between chunks. Each lane takes vectors l, l + 64, ... in increasing order
+// and then the head and tail elements, as gemv_unaligned does, so both give bitwise the
+// same result.
+// Two shapes of wave: R rows per wave, U vectors per lane and row per burst (the same bytes
+// in flight). One row per wave spreads the rows over more waves; two rows per wave halve
+// the LDS reads of x, which at larger M bound the kernel.
+struct ShiftShape {
+    int r, u;
+};
+constexpr ShiftShape kShiftShapes[2] = {{1, 4}, {2, 2}};
 
-template <int M>
-__global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes)
+template <int M, int R, int U>
+__global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes, int chunk)
 {
-    constexpr int R = kShiftRows, U = kShiftUnroll;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     u32x4 *xs = reinterpret_cast<u32x4 *>(lds);
     const int lane = threadIdx.x & 63;
@@ -523,9 +528,9 @@ __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes)
     const int waves = (int)(blockDim.x >> 6);
     const int cls = blockIdx.y;
     const int class_rows = (p.n - cls + classes - 1) / classes;
-    if (class_rows <= 0)   // fewer rows than classes: this workgroup has none (uniform exit)
+    const int blocks = (class_rows + waves * R - 1) / (waves * R);   // row blocks of the class
+    if ((int)blockIdx.x >= blocks)   // uniform per workgroup
         return;
-    const int j0 = (blockIdx.x * waves + wave) * R;
     const uint16_t *w_cls = p.w0 + (int64_t)cls * p.ldw0;
     const int h = (int)((8u - (unsigned)(((uintptr_t)w_cls >> 1) & 7u)) & 7u);
     const int ka = min(h, p.k);
@@ -536,12 +541,56 @@ __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes)
     for (int m = 0; m < M; ++m)
         q[m] = (int)((((uintptr_t)(p.x + (int64_t)m * p.ldx) >> 1) + (unsigned)h) & 7u);
 
-    const uint16_t *wr[R];
+    // Windows inside every row of X (vectors [vlo, vend)) are read without branches, SV per
+    // thread and row of X in flight before any is written; the at most two others element
+    // by element. Vectors [c0, c1) of every row of X go to xs[m * chunk + v - c0].
+    constexpr int SV = M <= 4 ? 4 : M <= 8 ? 2 : 1;
+    const int threads = (int)blockDim.x;
+    const int tid = (int)threadIdx.x;
+    const int vlo = ka >= 1 ? 0 : 1;
+    const int vhi = p.k - 10 - ka >= 0 ? ((p.k - 10 - ka) >> 3) + 1 : 0;
+    const int vend = min(nvec, vhi);
+    auto stage = [&](int c0, int c1) {
+        if (vend > vlo) {
+            const int i0 = max(c0, vlo), i1 = min(c1, vend);
+            for (int v0 = i0 + tid; v0 < i1; v0 += SV * threads) {
+                u32x4 t[SV][M];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {   // rows past the class re-read its last row, unstored
-        const int j = min(j0 + r, class_rows - 1);
-        wr[r] = p.w0 + (int64_t)(cls + classes * j) * p.ldw0 + ka;
-    }
+                for (int i = 0; i < SV; ++i) {
+                    const int vc = min(v0 + i * threads, i1 - 1);
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        t[i][m] = x_window_interior(p.x + (int64_t)m * p.ldx, ka + 8 * vc, q[m]);
+                }
+#pragma unroll
+                for (int i = 0; i < SV; ++i) {
+                    const int v = v0 + i * threads;
+                    if (v < i1) {
+#pragma unroll
+                        for (int m = 0; m < M; ++m)
+                            xs[m * chunk + v - c0] = t[i][m];
+                    }
+                }
+            }
+            // the edge vectors of the chunk: [c0, min(c1, vlo)) and [max(c0, vend), c1)
+            const int e1 = max(0, min(c1, vlo) - c0);
+            const int e2 = max(0, c1 - max(c0, vend));
+            for (int e = tid; e < e1 + e2; e += threads) {
+                const int v = e < e1 ? c0 + e : max(c0, vend) + (e - e1);
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    xs[m * chunk + v - c0] = x_window(p.x + (int64_t)m * p.ldx, ka + 8 * v, p.k, q[m]);
+            }
+        } else {
+            for (int v = c0 + tid; v < c1; v += threads) {
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    xs[m * chunk + v - c0] = x_window(p.x + (int64_t)m * p.ldx, ka + 8 * v, p.k, q[m]);
+            }
+        }
+    };
+
+    const uint16_t *wr[R];
     u32x4 wv[U][R];
     auto burst = [&](int s0) {
 #pragma unroll
@@ -550,115 +599,109 @@ __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes)
             for (int r = 0; r < R; ++r)
                 wv[u][r] = load_stream(wr[r] + 8 * min(s0 + lane + 64 * u, nvec - 1));
     };
-    if (nvec > 0)
-        burst(0);   // the first weights are in flight while x is staged
-
-    // Windows inside every row of X (vectors [vlo, vend)) are read without branches, SV per
-    // thread and row of X in flight before any is written; the at most two others element
-    // by element afterwards.
-    constexpr int SV = M <= 4 ? 4 : M <= 8 ? 2 : 1;
-    const int threads = (int)blockDim.x;
-    const int vlo = ka >= 1 ? 0 : 1;
-    const int vhi = p.k - 10 - ka >= 0 ? ((p.k - 10 - ka) >> 3) + 1 : 0;
-    const int vend = min(nvec, vhi);
-    const int tid = (int)threadIdx.x;
-    if (vend > vlo) {
-        for (int v0 = vlo + tid; v0 < vend; v0 += SV * threads) {
-            u32x4 t[SV][M];
-#pragma unroll
-            for (int i = 0; i < SV; ++i) {
-                const int vc = min(v0 + i * threads, vend - 1);
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    t[i][m] = x_window_interior(p.x + (int64_t)m * p.ldx, ka + 8 * vc, q[m]);
-            }
-#pragma unroll
-            for (int i = 0; i < SV; ++i) {
-                const int v = v0 + i * threads;
-                if (v < vend) {
-#pragma unroll
-                    for (int m = 0; m < M; ++m)
-                        xs[m * nvec + v] = t[i][m];
-                }
-            }
-        }
-        // the edge vectors: [0, vlo) and [vend, nvec), at most one each, one per thread
-        const int v = tid < vlo ? tid : vend + (tid - vlo);
-        if (v < nvec) {
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-                xs[m * nvec + v] = x_window(p.x + (int64_t)m * p.ldx, ka + 8 * v, p.k, q[m]);
-        }
-    } else {
-        for (int v = tid; v < nvec; v += threads) {
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-                xs[m * nvec + v] = x_window(p.x + (int64_t)m * p.ldx, ka + 8 * v, p.k, q[m]);
-        }
-    }
-    __syncthreads();
-
-    float acc[R][M];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            acc[r][m] = 0.f;
-    for (int s0 = 0; s0 < nvec; s0 += 64 * U) {
-        if (s0 > 0)
-            burst(s0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = s0 + lane + 64 * u;
-            const int vc = min(v, nvec - 1);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const u32x4 xv = xs[m * nvec + vc];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float next = dot8(wv[u][r], xv, acc[r][m]);
-                    acc[r][m] = v < nvec ? next : acc[r][m];
-                }
-            }
-        }
-    }
-    // Lanes 0..7 take the head elements, lanes 8..15 the tail elements.
-    const int kk = lane < 8 ? lane : tail_begin + (lane - 8);
-    const bool take = lane < 8 ? kk < ka : (lane < 16 && kk < p.k);
-    if (take) {
+    auto rows_of = [&](int blk) {   // rows past the class re-read its last row, unstored
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float w = bf16_to_f32(wr[r][kk - ka]);
+            const int j = min((blk * waves + wave) * R + r, class_rows - 1);
+            wr[r] = p.w0 + (int64_t)(cls + classes * j) * p.ldw0 + ka;
+        }
+    };
+
+    // When the M rows of x fit (chunk >= nvec) they are staged once and serve every row
+    // block this workgroup takes; otherwise each row block stages them chunk by chunk.
+    const bool once = chunk >= nvec;
+    rows_of(blockIdx.x);
+    if (nvec > 0)
+        burst(0);   // the first weights are in flight while x is staged
+    if (once) {
+        stage(0, nvec);
+        __syncthreads();
+    }
+    for (int blk = blockIdx.x;;) {
+        float acc[R][M];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int m = 0; m < M; ++m)
-                acc[r][m] = fmaf(w, bf16_to_f32(p.x[(int64_t)m * p.ldx + kk]), acc[r][m]);
-        }
-    }
-    float out = 0.f;
+                acc[r][m] = 0.f;
+        // chunk is a multiple of 64 * U (or covers the row), so every lane still meets its
+        // vectors l, l + 64, ... in increasing order, whatever the chunking.
+        for (int c0 = 0; c0 < nvec; c0 += chunk) {
+            const int c1 = min(nvec, c0 + chunk);
+            if (!once) {
+                if (c0 > 0)
+                    burst(c0);   // these weights are in flight while the chunk is staged
+                __syncthreads();   // every wave is done with the previous contents
+                stage(c0, c1);
+                __syncthreads();
+            }
+            for (int s0 = c0; s0 < c1; s0 += 64 * U) {
+                if (s0 > c0)
+                    burst(s0);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+                for (int u = 0; u < U; ++u) {
+                    const int v = s0 + lane + 64 * u;
+                    const int vc = min(v, c1 - 1);
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float sum = lane63(wave_sum(acc[r][m]));
-            if (lane == r * M + m)
-                out = sum;
+                    for (int m = 0; m < M; ++m) {
+                        const u32x4 xv = xs[m * chunk + vc - c0];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const float next = dot8(wv[u][r], xv, acc[r][m]);
+                            acc[r][m] = v < c1 ? next : acc[r][m];
+                        }
+                    }
+                }
+            }
         }
-    if (lane < R * M) {
-        const int r = lane / M, m = lane - (lane / M) * M;
-        if (j0 + r < class_rows)
-            p.y0[(int64_t)m * p.ldy0 + cls + classes * (j0 + r)] = out;
+        // Lanes 0..7 take the head elements, lanes 8..15 the tail elements.
+        const int kk = lane < 8 ? lane : tail_begin + (lane - 8);
+        const bool take = lane < 8 ? kk < ka : (lane < 16 && kk < p.k);
+        if (take) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float w = bf16_to_f32(wr[r][kk - ka]);
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    acc[r][m] = fmaf(w, bf16_to_f32(p.x[(int64_t)m * p.ldx + kk]), acc[r][m]);
+            }
+        }
+        float out = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float sum = lane63(wave_sum(acc[r][m]));
+                if (lane == r * M + m)
+                    out = sum;
+            }
+        const int j0 = (blk * waves + wave) * R;
+        if (lane < R * M) {
+            const int r = lane / M, m = lane - (lane / M) * M;
+            if (j0 + r < class_rows)
+                p.y0[(int64_t)m * p.ldy0 + cls + classes * (j0 + r)] = out;
+        }
+        blk += gridDim.x;
+        if (blk >= blocks)
+            break;
+        rows_of(blk);
+        if (nvec > 0)
+            burst(0);
     }
 }
 
-template <size_t... I>
+template <int S, size_t... I>
 std::array<const void *, GEMV_MAX_M> unaligned_lds_table(std::index_sequence<I...>)
 {
-    return {reinterpret_cast<const void *>(&gemv_unaligned_lds<(int)I + 1>)...};
+    return {reinterpret_cast<const void *>(
+        &gemv_unaligned_lds<(int)I + 1, kShiftShapes[S].r, kShiftShapes[S].u>)...};
 }
 
-const std::array<const void *, GEMV_MAX_M> kUnalignedLds =
-    unaligned_lds_table(std::make_index_sequence<GEMV_MAX_M>{});
+// [shape][M - 1]
+const std::array<const void *, GEMV_MAX_M> kUnalignedLds[2] = {
+    unaligned_lds_table<0>(std::make_index_sequence<GEMV_MAX_M>{}),
+    unaligned_lds_table<1>(std::make_index_sequence<GEMV_MAX_M>{})};
 
 // ---------------------------------------------------------------------------- dispatch
 // Kernel handles for hipLaunchKernel; fused instances take ArgsMulti, the others Args.
@@ -711,23 +754,36 @@ gemv_status device_error(hipError_t e) { return record_hip_error((int)e, GEMV_ER
 
 constexpr size_t kShiftMaxLds = 128 * 1024;   // staged x for the class-staged unaligned kernel
 
-// Launch an unsplit single-matrix unaligned call on gemv_unaligned_lds when the M shifted
-// x rows fit in LDS; *done tells whether it did.
+// Launch an unsplit single-matrix unaligned call on gemv_unaligned_lds; *done tells whether
+// it did. The staged chunk of x is the whole row when the M rows fit in kShiftMaxLds, else
+// the largest multiple of a burst (64 lanes x U vectors) that fits.
 gemv_status launch_unaligned_lds(gemv_plan_t p, const gemv_segment &seg, const void *X,
                                  int64_t ldx, void *stream, bool *done)
 {
     *done = false;
-    const size_t bytes = (size_t)p->m * (size_t)(p->k / 8) * sizeof(u32x4);
-    if (p->splits != 1 || bytes == 0 || bytes > kShiftMaxLds)
+    const int64_t vecs = p->k / 8;   // vectors per row of the class with the most
+    if (p->splits != 1 || vecs == 0)
         return GEMV_OK;
-    const void *fn = kUnalignedLds[p->m - 1];
-    static std::atomic<bool> allowed[GEMV_MAX_M + 1];
-    if (bytes > 64 * 1024 && !allowed[p->m].load(std::memory_order_acquire)) {
+    const int64_t per_vec = (int64_t)p->m * (int64_t)sizeof(u32x4);
+    // One row per wave up to M = 4, two above (measured at 4097 x 14337, M = 1..16).
+    const int shape = p->m <= 4 ? 0 : 1;
+    const ShiftShape sh = kShiftShapes[shape];
+    const int64_t burst = (int64_t)kWaveLanes * sh.u;
+    int64_t chunk_vecs = vecs;
+    if (vecs * per_vec > (int64_t)kShiftMaxLds)
+        chunk_vecs = (int64_t)kShiftMaxLds / per_vec / burst * burst;
+    if (chunk_vecs < 1)
+        return GEMV_OK;
+    int chunk = (int)chunk_vecs;
+    const size_t bytes = (size_t)(chunk_vecs * per_vec);
+    const void *fn = kUnalignedLds[shape][p->m - 1];
+    static std::atomic<bool> allowed[2][GEMV_MAX_M + 1];
+    if (bytes > 64 * 1024 && !allowed[shape][p->m].load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)kShiftMaxLds);
         if (e != hipSuccess)
             return device_error(e);
-        allowed[p->m].store(true, std::memory_order_release);
+        allowed[shape][p->m].store(true, std::memory_order_release);
     }
     *done = true;
     // Rows r and r + classes start at the same offset from the 16-byte grid.
@@ -741,7 +797,20 @@ gemv_status launch_unaligned_lds(gemv_plan_t p, const gemv_segment &seg, const v
         classes = 4;
     const int waves = 8;
     const int64_t class_rows = (p->n + classes - 1) / classes;
-    const int64_t blocks = (class_rows + (int64_t)kShiftRows * waves - 1) / ((int64_t)kShiftRows * waves);
+    int64_t blocks = (class_rows + (int64_t)sh.r * waves - 1) / ((int64_t)sh.r * waves);
+    // When x fits, workgroups take row blocks blockIdx.x, + gridDim.x, ...: no more of them
+    // per class than the classes' share of what the device holds at once, so none waits for
+    // a slot and x is staged once per workgroup. Chunked x is staged per row block anyway,
+    // and there one row block per workgroup measured faster.
+    if (chunk_vecs >= vecs) {
+        int per_cu = 0;
+        hipError_t oe = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn,
+                                                                     kWaveLanes * waves, bytes);
+        if (oe != hipSuccess)
+            return device_error(oe);
+        const int64_t resident = (int64_t)std::max(per_cu, 1) * p->dev.compute_units;
+        blocks = std::min(blocks, std::max<int64_t>(1, (resident + classes - 1) / classes));
+    }
     Args a;
     memset(&a, 0, sizeof a);
     a.w0 = static_cast<const uint16_t *>(seg.W);
@@ -754,8 +823,8 @@ gemv_status launch_unaligned_lds(gemv_plan_t p, const gemv_segment &seg, const v
     a.k = (int32_t)p->k;
     a.slice = (int32_t)p->k;
     a.waves = waves;
-    a.rows = kShiftRows;
-    void *args[] = {&a, &classes};
+    a.rows = sh.r;
+    void *args[] = {&a, &classes, &chunk};
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks, (unsigned)classes),
                                    dim3(kWaveLanes * waves), args, bytes,
                                    static_cast<hipStream_t>(stream));

@@ -51,3 +51,29 @@ def test_batch_unaligned(m):
     Y, _ = gemv(W, X)
     oracle_check(W, X, Y, f"unaligned m={m}")
     rows_match_batch_one(W, X, Y)
+
+
+@pytest.mark.parametrize("m,ldw", [(5, 14339), (9, 14340), (16, 14337)])
+def test_batch_unaligned_chunked(m, ldw):
+    """Unaligned rows whose M shifted x rows exceed the LDS the kernel stages them in: x goes
+    through in chunks, and every row of Y still equals its batch-1 run bitwise."""
+    n, k = 37, 14337
+    w, x = draw(n, k, m, seed=300 + m)
+    W = device_matrix(w, ld=ldw, offset=1)
+    X = device_matrix(x, ld=k + 3, offset=3)
+    Y, _ = gemv(W, X)
+    oracle_check(W, X, Y, f"unaligned chunked m={m}")
+    rows_match_batch_one(W, X, Y)
+
+
+@pytest.mark.parametrize("m", [1, 3, 7])
+def test_batch_unaligned_many_rows(m):
+    """More unaligned row blocks than the device holds at once: workgroups loop over row
+    blocks with x staged once, and the results are those of the oracle."""
+    n, k = 200_000, 301
+    w, x = draw(n, k, m, seed=400 + m)
+    W = device_matrix(w, ld=303, offset=1)
+    X = device_matrix(x, ld=k + 1, offset=1)
+    Y, _ = gemv(W, X)
+    oracle_check(W, X, Y, f"unaligned many rows m={m}")
+    rows_match_batch_one(W, X, Y)
