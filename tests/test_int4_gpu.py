@@ -38,7 +38,8 @@ def check(packed, scales, x, Y, what):
     return rep
 
 
-@pytest.mark.parametrize("n,k", [(4096, 14336), (1024, 4096), (6144, 4096), (28672, 4096)])
+@pytest.mark.parametrize("n,k", [(4096, 14336), (1024, 4096), (6144, 4096), (4096, 4096),
+                                 (28672, 4096), (128256, 4096)])
 def test_llama_shapes(n, k):
     packed, scales, _, x = draw(n, k, seed=n + k)
     Y, p = run(packed, scales, x)

@@ -42,7 +42,7 @@ def check(w, h, gain, Y, what, eps=EPS):
     return rep
 
 
-@pytest.mark.parametrize("segments", [(4096, 1024, 1024), (14336, 14336), (4096,)])
+@pytest.mark.parametrize("segments", [(4096, 1024, 1024), (14336, 14336), (4096,), (128256,)])
 def test_llama_projections(segments):
     k = 4096
     w, h, gain = draw(sum(segments), k, seed=sum(segments))
