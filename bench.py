@@ -466,7 +466,7 @@ def main(argv=None):
     log(f"device: {props.name} {arch} CUs={props.multi_processor_count}")
 
     # headline: down_proj 4096 x 14336, batch 1
-    cfg = workloads.CONFIGS[1]
+    cfg = workloads.DOWN_PROJ
     g = cfg.gemvs[0]
     (w, x), = workloads.draw_config(cfg)
     res, total, per, plan = bench_gemv(torch, bbd, g, w, x, args.steps, args.warmup)
@@ -526,17 +526,17 @@ def main(argv=None):
 
     if not args.skip_shapes:
         shapes = []
-        kproj = workloads.CONFIGS[0].gemvs[0]
-        wkp, xkp = workloads.draw_config(workloads.CONFIGS[0])[0]
+        kproj = workloads.K_PROJ_AND_TAILS.gemvs[0]
+        wkp, xkp = workloads.draw_config(workloads.K_PROJ_AND_TAILS)[0]
         shapes.append(("k_proj", kproj, wkp, xkp, ()))
-        for gg, (ww, xx) in zip(workloads.CONFIGS[2].gemvs, workloads.draw_config(workloads.CONFIGS[2])):
+        for gg, (ww, xx) in zip(workloads.FUSED_PROJECTIONS.gemvs, workloads.draw_config(workloads.FUSED_PROJECTIONS)):
             shapes.append((gg.name + "_fused", gg, ww, xx, gg.segments))
         o = workloads.Gemv("o_proj", 4096, 4096)
         shapes.append(("o_proj", o, *workloads.draw_gemv(o, workloads.generator(7)), ()))
         lm = workloads.Gemv("lm_head", workloads.VOCAB, workloads.HIDDEN)
         shapes.append(("lm_head", lm, *workloads.draw_gemv(lm, workloads.generator(8, "cuda"), "cuda"),
                        ()))
-        for gg, (ww, xx) in zip(workloads.CONFIGS[4].gemvs, workloads.draw_config(workloads.CONFIGS[4])):
+        for gg, (ww, xx) in zip(workloads.SKINNY_BATCH.gemvs, workloads.draw_config(workloads.SKINNY_BATCH)):
             shapes.append((gg.name, gg, ww, xx, ()))
         for name, gg, ww, xx, segs in shapes:
             r, _, _, _ = bench_gemv(torch, bbd, gg, ww, xx, args.shape_steps, 10, segs)

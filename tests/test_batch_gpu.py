@@ -20,7 +20,7 @@ def rows_match_batch_one(W, X, Y):
 
 
 def test_skinny_config():
-    cfg = workloads.CONFIGS[4]
+    cfg = workloads.SKINNY_BATCH
     for g, (w, x) in zip(cfg.gemvs, workloads.draw_config(cfg)):
         W, X = device_matrix(w), device_matrix(x)
         Y, p = gemv(W, X)

@@ -54,7 +54,7 @@ def test_algorithmic_bytes_of_the_workloads():
     assert bench.alg_bytes(4097, 14337, 3) == 117_612_564
     step = sum(bench.alg_bytes(g.n, g.k, g.m) for g in workloads.decode_step_gemvs())
     assert step == 15_017_047_040
-    for cfg in workloads.CONFIGS:
+    for cfg in workloads.WORKLOADS:
         for g in cfg.gemvs:
             assert g.alg_bytes == bench.alg_bytes(g.n, g.k, g.m)
 

@@ -33,7 +33,7 @@ def fused_vs_concat(parts, x, ldws=None, ldys=None):
 
 
 def test_qkv_and_gate_up():
-    cfg = workloads.CONFIGS[2]
+    cfg = workloads.FUSED_PROJECTIONS
     for g, (w, x) in zip(cfg.gemvs, workloads.draw_config(cfg)):
         parts = list(torch.split(w, list(g.segments), 0))
         plan = fused_vs_concat(parts, x)

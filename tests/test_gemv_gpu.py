@@ -31,7 +31,7 @@ def small_ints(shape, seed):
 # ---------------------------------------------------------------------------- workloads
 def test_k_proj_and_tails():
     """k_proj 1024x4096 with tails 7x129 and 33x1000, drawn in order from seed 1000."""
-    cfg = workloads.CONFIGS[0]
+    cfg = workloads.K_PROJ_AND_TAILS
     for g, (w, x) in zip(cfg.gemvs, workloads.draw_config(cfg)):
         W, X = device_matrix(w), device_matrix(x)
         Y, p = gemv(W, X)
@@ -41,7 +41,7 @@ def test_k_proj_and_tails():
 
 def test_down_proj_full_size():
     """The split-K stress shape, 4096x14336, in the launch configuration the bench times."""
-    cfg = workloads.CONFIGS[1]
+    cfg = workloads.DOWN_PROJ
     (w, x), = workloads.draw_config(cfg)
     W, X = device_matrix(w), device_matrix(x)
     Y, p = gemv(W, X)

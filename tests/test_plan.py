@@ -52,7 +52,7 @@ def test_grid_arithmetic_matches_h100_tiles():
     assert math.ceil(lm["rows"] / lm["rows_per_tile"]) > lm["programs_more_than"]
 
 
-SHAPES = [(g.n, g.k, g.m) for cfg in workloads.CONFIGS for g in cfg.gemvs]
+SHAPES = [(g.n, g.k, g.m) for cfg in workloads.WORKLOADS for g in cfg.gemvs]
 
 
 @pytest.mark.parametrize("n,k,m", sorted(set(SHAPES)))

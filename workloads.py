@@ -45,13 +45,9 @@ class Gemv:
 
 @dataclass(frozen=True)
 class Config:
-    index: int
+    seed: int
     title: str
     gemvs: tuple[Gemv, ...] = field(default_factory=tuple)
-
-    @property
-    def seed(self) -> int:
-        return 1000 + self.index
 
 
 def decode_step_gemvs(layers: int = LAYERS) -> tuple[Gemv, ...]:
@@ -68,20 +64,27 @@ def decode_step_gemvs(layers: int = LAYERS) -> tuple[Gemv, ...]:
     return tuple(seq)
 
 
-CONFIGS: tuple[Config, ...] = (
-    Config(0, "k_proj GEMV 1024x4096 with tails 7x129 and 33x1000, batch 1",
-           (Gemv("k_proj", KV_ROWS, HIDDEN), Gemv("tail_7x129", 7, 129), Gemv("tail_33x1000", 33, 1000))),
-    Config(1, "split-K stress GEMV, down_proj 4096x14336, batch 1",
-           (Gemv("down", HIDDEN, INTERMEDIATE),)),
-    Config(2, "fused projections at batch 1: QKV 6144x4096 and gate_up 28672x4096",
-           (Gemv("qkv", Q_ROWS + 2 * KV_ROWS, HIDDEN, segments=(Q_ROWS, KV_ROWS, KV_ROWS)),
-            Gemv("gate_up", 2 * INTERMEDIATE, HIDDEN, segments=(INTERMEDIATE, INTERMEDIATE)))),
-    Config(3, "full batch-1 decode-step GEMV sequence (32 layers + lm_head) in one graph",
-           decode_step_gemvs()),
-    Config(4, "skinny-batch GEMV 4096x14336 at M in {1,2,4,8,16}, tail 4097x14337 at M=3",
-           tuple(Gemv(f"skinny_m{m}", HIDDEN, INTERMEDIATE, m) for m in (1, 2, 4, 8, 16))
-           + (Gemv("skinny_tail_m3", HIDDEN + 1, INTERMEDIATE + 1, 3),)),
-)
+K_PROJ_AND_TAILS = Config(
+    1000, "k_proj GEMV 1024x4096 with tails 7x129 and 33x1000, batch 1",
+    (Gemv("k_proj", KV_ROWS, HIDDEN), Gemv("tail_7x129", 7, 129), Gemv("tail_33x1000", 33, 1000)))
+DOWN_PROJ = Config(
+    1001, "split-K stress GEMV, down_proj 4096x14336, batch 1",
+    (Gemv("down", HIDDEN, INTERMEDIATE),))
+FUSED_PROJECTIONS = Config(
+    1002, "fused projections at batch 1: QKV 6144x4096 and gate_up 28672x4096",
+    (Gemv("qkv", Q_ROWS + 2 * KV_ROWS, HIDDEN, segments=(Q_ROWS, KV_ROWS, KV_ROWS)),
+     Gemv("gate_up", 2 * INTERMEDIATE, HIDDEN, segments=(INTERMEDIATE, INTERMEDIATE))))
+DECODE_STEP = Config(
+    1003, "full batch-1 decode-step GEMV sequence (32 layers + lm_head) in one graph",
+    decode_step_gemvs())
+SKINNY_BATCH = Config(
+    1004, "skinny-batch GEMV 4096x14336 at M in {1,2,4,8,16}, tail 4097x14337 at M=3",
+    tuple(Gemv(f"skinny_m{m}", HIDDEN, INTERMEDIATE, m) for m in (1, 2, 4, 8, 16))
+    + (Gemv("skinny_tail_m3", HIDDEN + 1, INTERMEDIATE + 1, 3),))
+
+# Every workload above, smallest first.
+WORKLOADS: tuple[Config, ...] = (K_PROJ_AND_TAILS, DOWN_PROJ, FUSED_PROJECTIONS, DECODE_STEP,
+                                 SKINNY_BATCH)
 
 
 def generator(seed: int, device: str | torch.device = "cpu") -> torch.Generator:
@@ -124,7 +127,7 @@ def draw_decode_step(device: str | torch.device = "cuda", layers: int = LAYERS,
     Returns a list of (Gemv, [W parts], X). About 15 GB of weights at 32 layers, so draw on
     the GPU.
     """
-    gen = generator(CONFIGS[3].seed if seed is None else seed, device)
+    gen = generator(DECODE_STEP.seed if seed is None else seed, device)
     out = []
     for g in decode_step_gemvs(layers):
         w, x = draw_gemv(g, gen, device)
