@@ -111,7 +111,8 @@ SIGNATURES = {
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python bandwidth_bound_decode_amd/build.py` "
                           "(the GEMV has no fallback path)")
     so = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
