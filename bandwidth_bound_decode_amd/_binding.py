@@ -224,6 +224,26 @@ def _row_stride(t: torch.Tensor, what: str) -> int:
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
+def _on_gpu(what: str, *tensors: torch.Tensor):
+    """Every tensor argument is handed to the kernels as a device pointer: refuse host
+    tensors (and tensors on different devices) before anything is launched."""
+    dev = None
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError(f"{what}: every tensor must be on the GPU (got {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{what}: tensors on different devices ({dev}, {t.device})")
+
+
+def _need(t: torch.Tensor, rows: int, cols: int, what: str):
+    """t must hold at least `rows` rows of at least `cols` elements ([cols] when rows == 1)."""
+    r, c = (1, t.shape[0]) if t.dim() == 1 else (t.shape[0], t.shape[1])
+    if r < rows or c < cols:
+        raise ValueError(f"{what} is {tuple(t.shape)}, the plan needs [{rows}, {cols}]")
+
+
 def _ws(workspace):
     if workspace is None:
         return None, 0
@@ -236,6 +256,12 @@ def run(plan: Plan, W: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
     Y fp32 [m, n] or [n]. Returns Y."""
     if W.dtype != torch.bfloat16 or X.dtype != torch.bfloat16 or Y.dtype != torch.float32:
         raise TypeError("W and X must be bfloat16 and Y float32")
+    _on_gpu("gemv_run", W, X, Y, *([workspace] if workspace is not None else []))
+    if W.dim() != 2 or W.shape[0] != plan.n:
+        raise ValueError(f"W is {tuple(W.shape)}, the plan has {plan.n} rows")
+    _need(W, plan.n, plan.k, "W")
+    _need(X, plan.m, plan.k, "X")
+    _need(Y, plan.m, plan.n, "Y")
     ws_ptr, ws_bytes = _ws(workspace)
     st = _lib.gemv_run(plan.handle, W.data_ptr(), _row_stride(W, "W"), X.data_ptr(),
                        _row_stride(X, "X"), Y.data_ptr(), _row_stride(Y, "Y"), ws_ptr,
@@ -252,6 +278,11 @@ def run_int4(plan: Plan, Wq: torch.Tensor, S: torch.Tensor, X: torch.Tensor, Y: 
     if Wq.dtype != torch.uint8 or S.dtype != torch.bfloat16 or X.dtype != torch.bfloat16 or \
             Y.dtype != torch.float32:
         raise TypeError("Wq must be uint8, S and X bfloat16, Y float32")
+    _on_gpu("gemv_int4_run", Wq, S, X, Y)
+    _need(Wq, plan.n, (plan.k + 1) // 2, "Wq")
+    _need(S, plan.n, (plan.k + 127) // 128, "S")
+    _need(X, 1, plan.k, "X")
+    _need(Y, 1, plan.n, "Y")
     st = _lib.gemv_int4_run(plan.handle, Wq.data_ptr(), _row_stride(Wq, "Wq"), S.data_ptr(),
                             _row_stride(S, "S"), X.data_ptr(), Y.data_ptr(),
                             _stream_handle(stream))
@@ -274,6 +305,12 @@ def rmsnorm_run(plan: Plan, segments, H: torch.Tensor, gamma: torch.Tensor, eps:
                          w.shape[0])
     if H.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16:
         raise TypeError("H and gamma must be bfloat16")
+    _on_gpu("gemv_rmsnorm_run", H, gamma, *[t for pair in segs for t in pair])
+    _need(H, 1, plan.k, "H")
+    _need(gamma, 1, plan.k, "gamma")
+    for w, y in segs:
+        _need(w, w.shape[0], plan.k, "segment W")
+        _need(y, 1, w.shape[0], "segment Y")
     st = _lib.gemv_rmsnorm_run(plan.handle, arr, len(segs), H.data_ptr(), gamma.data_ptr(),
                                float(eps), _stream_handle(stream))
     _check(st, "gemv_rmsnorm_run")
@@ -291,6 +328,12 @@ def fused_run(plan: Plan, segments, X: torch.Tensor, workspace: torch.Tensor | N
                          _row_stride(y, "Y") if y.dim() == 2 else w.shape[0])
     if X.dtype != torch.bfloat16:
         raise TypeError("X must be bfloat16")
+    _on_gpu("gemv_fused_run", X, *[t for pair in segs for t in pair],
+            *([workspace] if workspace is not None else []))
+    _need(X, plan.m, plan.k, "X")
+    for w, y in segs:
+        _need(w, w.shape[0], plan.k, "segment W")
+        _need(y, plan.m, w.shape[0], "segment Y")
     ws_ptr, ws_bytes = _ws(workspace)
     st = _lib.gemv_fused_run(plan.handle, arr, len(segs), X.data_ptr(), _row_stride(X, "X"),
                              ws_ptr, ws_bytes, _stream_handle(stream))
@@ -366,6 +409,10 @@ class Chain:
                                   w.shape[0])
             if x.dtype != torch.bfloat16:
                 raise TypeError("chain inputs must be bfloat16")
+            _on_gpu("gemv_chain_create", x, *[t for pair in segments for t in pair])
+            for w, y in segments:
+                _need(w, w.shape[0], x.shape[-1], "chain W")
+                _need(y, 1, w.shape[0], "chain Y")
             self._keep.append(segs)
             arr[i] = ChainLink(segs, len(segments), x.data_ptr(), x.shape[-1])
         if device is None:

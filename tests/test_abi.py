@@ -223,3 +223,30 @@ def test_chain_validation_before_any_hip_call():
     assert lib.gemv_chain_run(None, None) == Status.INVALID_ARG
     assert lib.gemv_chain_check(None) == Status.INVALID_ARG
     lib.gemv_chain_destroy(None)
+
+
+def test_binding_refuses_host_tensors_and_short_buffers():
+    """The binding hands data pointers to the kernels as device pointers: host tensors and
+    buffers smaller than the plan are refused before any call reaches the library."""
+    import torch
+
+    import bandwidth_bound_decode_amd as bbd
+
+    plan = bbd.Plan(64, 256, 2, desc=(256, 8.0e12, 1.0e-6))   # host-only plan
+    W = torch.zeros((64, 256), dtype=torch.bfloat16)
+    X = torch.zeros((2, 256), dtype=torch.bfloat16)
+    Y = torch.zeros((2, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="on the GPU"):
+        bbd.run(plan, W, X, Y)
+    with pytest.raises(ValueError, match="on the GPU"):
+        bbd.fused_run(plan, [(W[:32], Y[:, :32]), (W[32:], Y[:, 32:])], X)
+    with pytest.raises(TypeError):
+        bbd.run(plan, W.float(), X, Y)
+    # shape checks are exercised with the device check bypassed
+    from bandwidth_bound_decode_amd import _binding as b
+    with pytest.raises(ValueError, match="the plan needs"):
+        b._need(X[:1], plan.m, plan.k, "X")
+    with pytest.raises(ValueError, match="the plan needs"):
+        b._need(Y[:, :63], plan.m, plan.n, "Y")
+    b._need(X, plan.m, plan.k, "X")
+    b._need(torch.zeros(256, dtype=torch.bfloat16), 1, 256, "X")
