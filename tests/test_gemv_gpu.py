@@ -291,3 +291,37 @@ def test_a_million_rows():
         Y, p = gemv(W, X)
         print(m, p.info, flush=True)
         oracle_check(W, X, Y, f"n=2^20 m={m}")
+
+
+def test_device_plans_equal_host_plans():
+    """gemv_plan on the GPU describes the device as the host-only planner is told to (CU
+    count from the runtime, 8 TB/s, the default latency): every workload shape, batch-1
+    INT4 and the RMSNorm prologue get the same plan both ways. The one field allowed to
+    differ is the LDS reserved only to cap resident workgroups (when a cap is set): the device plan confirms its size
+    with the runtime's occupancy calculator (256-byte steps), the host plan assumes a 512-byte
+    allocation unit; both must admit the same number of workgroups per CU."""
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    desc = (props.multi_processor_count, 8.0e12, 1.0e-6)
+    lds_per_cu = 160 * 1024
+
+    def same(a, b, what):
+        a, b = dict(a), dict(b)
+        la, lb = a.pop("lds_bytes"), b.pop("lds_bytes")
+        assert a == b, what
+        if not a["waves_per_cu"]:          # LDS that holds data (staged x), not a cap
+            assert la == lb, what
+            return
+        blocks = a["waves_per_cu"] // a["waves_per_block"]
+        for lds in (la, lb):
+            assert blocks * lds <= lds_per_cu < (blocks + 1) * lds, (what, lds, blocks)
+
+    shapes = [(g.n, g.k, g.m) for cfg in workloads.WORKLOADS for g in cfg.gemvs]
+    for n, k, m in sorted(set(shapes)):
+        same(bbd.Plan(n, k, m).info, bbd.Plan(n, k, m, desc=desc).info, (n, k, m))
+    for n in (4096, 28672, 128256):
+        same(bbd.Plan(n, 4096, 1, weights="int4").info,
+             bbd.Plan(n, 4096, 1, weights="int4", desc=desc).info, ("int4", n))
+        same(bbd.Plan(n, 4096, 1, prologue="rmsnorm").info,
+             bbd.Plan(n, 4096, 1, prologue="rmsnorm", desc=desc).info, ("rmsnorm", n))
