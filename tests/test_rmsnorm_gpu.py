@@ -63,6 +63,21 @@ def test_ragged_every_tile(n, k):
             assert bits_equal(Y, Y2), "not reproducible"
 
 
+def test_longest_k():
+    """K = 16368, the longest row the prologue accepts (its staging fills the 64 KiB of LDS a
+    workgroup gets by default): every burst length on 8-wave workgroups meets the tolerance,
+    and a single-wave workgroup, whose longer sum-of-squares chain would break the depth
+    bound, is refused by the planner rather than run."""
+    n, k = 65, 16368
+    w, h, gain = draw(n, k, seed=3 * n + k)
+    for u in (1, 2, 4, 8):
+        Y, p = run([w], h, gain, unroll=u, waves_per_block=8)
+        assert p.info["depth_bound"] <= 160
+        check(w, h, gain, Y, f"k={k} U={u}")
+    with pytest.raises(bbd.GemvError):
+        bbd.Plan(n, k, 1, prologue="rmsnorm", waves_per_block=1)
+
+
 def test_unit_scale_equals_gemv_run():
     """gamma = 1 and h in {+-1, +-1/2} with eps = 1 - mean(h^2): every step of the norm is
     exact, rms_inv = 1, and the result must be gemv_run's bit for bit."""
