@@ -803,11 +803,21 @@ gemv_status launch_unaligned_lds(gemv_plan_t p, const gemv_segment &seg, const v
     // a slot and x is staged once per workgroup. Chunked x is staged per row block anyway,
     // and there one row block per workgroup measured faster.
     if (chunk_vecs >= vecs) {
+        // The occupancy query, cached per kernel for the last LDS size asked about (one
+        // 64-bit word: bytes in the high half, workgroups per CU in the low half).
+        static std::atomic<uint64_t> occ[2][GEMV_MAX_M + 1];
+        const uint64_t seen = occ[shape][p->m].load(std::memory_order_relaxed);
         int per_cu = 0;
-        hipError_t oe = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn,
-                                                                     kWaveLanes * waves, bytes);
-        if (oe != hipSuccess)
-            return device_error(oe);
+        if (seen >> 32 == (uint64_t)bytes) {
+            per_cu = (int)(seen & 0xFFFFFFFFu);
+        } else {
+            hipError_t oe = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, fn, kWaveLanes * waves, bytes);
+            if (oe != hipSuccess)
+                return device_error(oe);
+            occ[shape][p->m].store(((uint64_t)bytes << 32) | (uint32_t)per_cu,
+                                   std::memory_order_relaxed);
+        }
         const int64_t resident = (int64_t)std::max(per_cu, 1) * p->dev.compute_units;
         blocks = std::min(blocks, std::max<int64_t>(1, (resident + classes - 1) / classes));
     }
