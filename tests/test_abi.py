@@ -250,3 +250,20 @@ def test_binding_refuses_host_tensors_and_short_buffers():
         b._need(Y[:, :63], plan.m, plan.n, "Y")
     b._need(X, plan.m, plan.k, "X")
     b._need(torch.zeros(256, dtype=torch.bfloat16), 1, 256, "X")
+
+
+def test_package_fails_loudly_without_the_library(tmp_path):
+    """With the compiled library absent the package refuses to import: there is no CPU or
+    Python fallback path. Checked in a child process on a copy of the package whose lib/
+    directory is empty."""
+    import shutil
+    import sys
+
+    pkg = os.path.join(ROOT, "bandwidth_bound_decode_amd")
+    copy = tmp_path / "bandwidth_bound_decode_amd"
+    shutil.copytree(pkg, copy, ignore=shutil.ignore_patterns("lib", "__pycache__"))
+    (copy / "lib").mkdir()
+    proc = subprocess.run([sys.executable, "-c", "import bandwidth_bound_decode_amd"],
+                          cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert proc.returncode != 0
+    assert "ImportError" in proc.stderr and "no fallback" in proc.stderr, proc.stderr[-500:]
