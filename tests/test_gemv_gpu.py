@@ -232,6 +232,33 @@ def test_one_workspace_shared_by_two_plans():
     assert not ws[:4 * 4096].any(), "tickets must be back at zero after the calls"
 
 
+def test_one_plan_on_two_streams_at_once():
+    """Calls on one split plan may run concurrently when each has its own workspace: two
+    streams, each with its own workspace, input and output, launch the same plan in turn
+    without synchronising, and every output is bitwise the sequential one."""
+    p = bbd.Plan(512, 14336, 2, splits=4)
+    assert p.info["splits"] == 4 and p.workspace_size > 0
+    ins = [draw(512, 14336, 2, seed=40 + i) for i in range(2)]
+    Ws = [device_matrix(w) for w, _ in ins]
+    Xs = [device_matrix(x) for _, x in ins]
+    ref = []
+    for W, X in zip(Ws, Xs):
+        Y, _ = gemv(W, X, plan=p)
+        oracle_check(W, X, Y, "sequential")
+        ref.append(Y.clone())
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    wss = [p.alloc_workspace() for _ in range(2)]
+    Ys = [output(2, 512) for _ in range(2)]
+    torch.cuda.synchronize()
+    for _ in range(20):
+        for i in range(2):
+            bbd.run(p, Ws[i], Xs[i], Ys[i], wss[i], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert bits_equal(Ys[i], ref[i]), f"stream {i} differs from the sequential run"
+        assert not wss[i][:4 * 4096].any(), "tickets must be back at zero"
+
+
 # ---------------------------------------------------------------------------- edges
 def test_degenerate_shapes():
     for n, k, m in ((1, 1, 1), (1, 8, 1), (1, 9, 2), (64, 1, 16), (1, 14336, 1), (2, 512, 1)):
