@@ -305,6 +305,22 @@ def pin_rmsnorm_closed_forms(so):
     assert np.allclose(y[0], want, rtol=1e-15, atol=0), "one nonzero h"
 
 
+def pin_rmsnorm_scale_invariance(so):
+    """With eps = 0 the normalisation cancels any power-of-two scale of h exactly: the sum of
+    squares scales by 4^j, its square root by 2^j and the dot product by 2^j, and scaling by
+    powers of two commutes with fp64 rounding. So y(2^j h) equals y(h) bit for bit (a mean of
+    |h| instead of h^2, a missing square root or a missing scale would all break it)."""
+    rng = np.random.default_rng(77)
+    n, k = 9, 200
+    w = _rand_bits(rng, (n, k), 0.02)
+    gain = _rand_bits(rng, (k,), 1.0)
+    hv = torch.tensor(rng.standard_normal(k)).to(torch.bfloat16).to(torch.float64).numpy()
+    base, _ = oracle.gemv_rmsnorm(w, _bf16_bits(hv), gain, 0.0, so=so)
+    for j in (-3, 1, 5):
+        y, _ = oracle.gemv_rmsnorm(w, _bf16_bits(hv * 2.0 ** j), gain, 0.0, so=so)
+        assert np.array_equal(y, base), f"rmsnorm scale invariance 2^{j}"
+
+
 def pin_rmsnorm_brute_force(so):
     """Exact rationals where eps makes mean(h^2) + eps a perfect square s^2: rms_inv = 1/s
     exactly, so the whole result is rational."""
@@ -332,7 +348,7 @@ def pin_rmsnorm_brute_force(so):
 PINS = (pin_bf16_decode, pin_identity, pin_one_hot, pin_constant_w, pin_brute_force,
         pin_cancellation, pin_numpy_matmul, pin_thread_invariance, pin_q4_format,
         pin_q4_equals_bf16_oracle, pin_q4_brute_force, pin_rmsnorm_unit_scale_is_plain_gemv,
-        pin_rmsnorm_closed_forms, pin_rmsnorm_brute_force)
+        pin_rmsnorm_closed_forms, pin_rmsnorm_scale_invariance, pin_rmsnorm_brute_force)
 
 
 def run_all(lib_path: str) -> int:

@@ -88,6 +88,7 @@ MUTATIONS = {
     "norm_gamma_dropped": ("(bf16_value(G[i]) * bf16_value(H[i]))", "bf16_value(H[i])"),
     "norm_no_sqrt": ("1.0 / sqrt(squares / (double)K + eps)", "1.0 / (squares / (double)K + eps)"),
     "norm_scale_missing": ("Y[row] = rms_inv * dot;", "Y[row] = dot;"),
+    "norm_abs_not_square": ("squares += hv * hv;", "squares += fabs(hv);"),
 }
 
 
