@@ -103,13 +103,22 @@ __global__ void __launch_bounds__(512) gemv_rmsnorm(NormArgs a)
     int blk = blockIdx.x;
     NormRow nr = norm_row(a, blk * waves + wave);
     u32x4 wv[U];
+    // Vector loads retire in order. When every thread stages exactly one vector (the decode
+    // shapes), its h and gamma loads go out before the first weight burst, so the staging
+    // waits for them only; otherwise the burst goes first.
+    const bool one = vecs == (int)blockDim.x;
+    u32x4 h0 = {0, 0, 0, 0}, g0 = {0, 0, 0, 0};
+    if (one) {
+        h0 = load_cached(a.h + kVecElems * (int)threadIdx.x);
+        g0 = load_cached(a.gamma + kVecElems * (int)threadIdx.x);
+    }
     norm_burst<U>(nr.w, 0, vecs, lane, wv);
 
     // u = gamma * h as hi + lo in LDS, and this thread's share of sum h^2.
     float sq = 0.f;
     for (int v = (int)threadIdx.x; v < vecs; v += (int)blockDim.x) {
-        const u32x4 hv = load_cached(a.h + kVecElems * v);
-        const u32x4 gv = load_cached(a.gamma + kVecElems * v);
+        const u32x4 hv = one ? h0 : load_cached(a.h + kVecElems * v);
+        const u32x4 gv = one ? g0 : load_cached(a.gamma + kVecElems * v);
         const unsigned hd[4] = {hv.x, hv.y, hv.z, hv.w};
         const unsigned gd[4] = {gv.x, gv.y, gv.z, gv.w};
         unsigned hi[4], lo[4];
