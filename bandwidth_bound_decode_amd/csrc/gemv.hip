@@ -550,27 +550,44 @@ __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes, i
     const int vlo = ka >= 1 ? 0 : 1;
     const int vhi = p.k - 10 - ka >= 0 ? ((p.k - 10 - ka) >> 3) + 1 : 0;
     const int vend = min(nvec, vhi);
-    auto stage = [&](int c0, int c1) {
+    // after_first() (the chunk's first weight burst) is issued right after the first batch
+    // of x loads: vector loads retire in order, so the x writes then wait for x only. The
+    // first pass runs on every lane (its loads are clamped), so the burst is wave-uniform.
+    auto stage = [&](int c0, int c1, auto &&after_first) {
+        bool first = true;
         if (vend > vlo) {
             const int i0 = max(c0, vlo), i1 = min(c1, vend);
-            for (int v0 = i0 + tid; v0 < i1; v0 += SV * threads) {
-                u32x4 t[SV][M];
+            if (i1 > i0) {
+                int v0 = i0 + tid;
+                do {
+                    u32x4 t[SV][M];
 #pragma unroll
-                for (int i = 0; i < SV; ++i) {
-                    const int vc = min(v0 + i * threads, i1 - 1);
-#pragma unroll
-                    for (int m = 0; m < M; ++m)
-                        t[i][m] = x_window_interior(p.x + (int64_t)m * p.ldx, ka + 8 * vc, q[m]);
-                }
-#pragma unroll
-                for (int i = 0; i < SV; ++i) {
-                    const int v = v0 + i * threads;
-                    if (v < i1) {
+                    for (int i = 0; i < SV; ++i) {
+                        const int vc = min(v0 + i * threads, i1 - 1);
 #pragma unroll
                         for (int m = 0; m < M; ++m)
-                            xs[m * chunk + v - c0] = t[i][m];
+                            t[i][m] = x_window_interior(p.x + (int64_t)m * p.ldx, ka + 8 * vc,
+                                                        q[m]);
                     }
-                }
+                    if (first) {
+                        after_first();
+                        first = false;
+                    }
+#pragma unroll
+                    for (int i = 0; i < SV; ++i) {
+                        const int v = v0 + i * threads;
+                        if (v < i1) {
+#pragma unroll
+                            for (int m = 0; m < M; ++m)
+                                xs[m * chunk + v - c0] = t[i][m];
+                        }
+                    }
+                    v0 += SV * threads;
+                } while (v0 < i1);
+            }
+            if (first) {
+                after_first();
+                first = false;
             }
             // the edge vectors of the chunk: [c0, min(c1, vlo)) and [max(c0, vend), c1)
             const int e1 = max(0, min(c1, vlo) - c0);
@@ -582,6 +599,7 @@ __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes, i
                     xs[m * chunk + v - c0] = x_window(p.x + (int64_t)m * p.ldx, ka + 8 * v, p.k, q[m]);
             }
         } else {
+            after_first();
             for (int v = c0 + tid; v < c1; v += threads) {
 #pragma unroll
                 for (int m = 0; m < M; ++m)
@@ -611,11 +629,14 @@ __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes, i
     // block this workgroup takes; otherwise each row block stages them chunk by chunk.
     const bool once = chunk >= nvec;
     rows_of(blockIdx.x);
-    if (nvec > 0)
-        burst(0);   // the first weights are in flight while x is staged
     if (once) {
-        stage(0, nvec);
+        stage(0, nvec, [&] {
+            if (nvec > 0)
+                burst(0);   // the first weights are in flight while x is staged
+        });
         __syncthreads();
+    } else if (nvec > 0) {
+        burst(0);
     }
     for (int blk = blockIdx.x;;) {
         float acc[R][M];
@@ -629,10 +650,12 @@ __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes, i
         for (int c0 = 0; c0 < nvec; c0 += chunk) {
             const int c1 = min(nvec, c0 + chunk);
             if (!once) {
+                // Chunks: the burst goes out before the barrier, while other waves finish
+                // the previous chunk (measured faster here than after the first x loads).
                 if (c0 > 0)
-                    burst(c0);   // these weights are in flight while the chunk is staged
+                    burst(c0);
                 __syncthreads();   // every wave is done with the previous contents
-                stage(c0, c1);
+                stage(c0, c1, [] {});
                 __syncthreads();
             }
             for (int s0 = c0; s0 < c1; s0 += 64 * U) {
