@@ -215,13 +215,23 @@ def _stream_handle(stream) -> int:
 
 
 def _row_stride(t: torch.Tensor, what: str) -> int:
+    """Row stride in elements of a 1-D (one row) or 2-D tensor whose rows are contiguous.
+    A strided view (buf[::2], M[:, j]) would be read by the kernels as if it were dense,
+    so it is refused."""
+    if t.dim() not in (1, 2):
+        raise ValueError(f"{what} must be 1-D or 2-D")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{what} rows must be contiguous (stride {t.stride(-1)} along the row)")
     if t.dim() == 1:
         return t.shape[0]
-    if t.dim() != 2:
-        raise ValueError(f"{what} must be 1-D or 2-D")
-    if t.shape[1] > 1 and t.stride(1) != 1:
-        raise ValueError(f"{what} rows must be contiguous")
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _vector(t: torch.Tensor, what: str):
+    """A single-row operand handed over as one pointer: [k] or [1, k], contiguous."""
+    if t.dim() == 2 and t.shape[0] != 1:
+        raise ValueError(f"{what} must be [k] or [1, k], got {tuple(t.shape)}")
+    _row_stride(t, what)
 
 
 def _on_gpu(what: str, *tensors: torch.Tensor):
@@ -283,6 +293,8 @@ def run_int4(plan: Plan, Wq: torch.Tensor, S: torch.Tensor, X: torch.Tensor, Y: 
     _need(S, plan.n, (plan.k + 127) // 128, "S")
     _need(X, 1, plan.k, "X")
     _need(Y, 1, plan.n, "Y")
+    _vector(X, "X")
+    _vector(Y, "Y")
     st = _lib.gemv_int4_run(plan.handle, Wq.data_ptr(), _row_stride(Wq, "Wq"), S.data_ptr(),
                             _row_stride(S, "S"), X.data_ptr(), Y.data_ptr(),
                             _stream_handle(stream))
@@ -301,8 +313,11 @@ def rmsnorm_run(plan: Plan, segments, H: torch.Tensor, gamma: torch.Tensor, eps:
     for i, (w, y) in enumerate(segs):
         if w.dtype != torch.bfloat16 or y.dtype != torch.float32:
             raise TypeError("segment W must be bfloat16 and Y float32")
+        _vector(y, "segment Y")
         arr[i] = Segment(w.data_ptr(), w.shape[0], _row_stride(w, "W"), y.data_ptr(),
                          w.shape[0])
+    _vector(H, "H")
+    _vector(gamma, "gamma")
     if H.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16:
         raise TypeError("H and gamma must be bfloat16")
     _on_gpu("gemv_rmsnorm_run", H, gamma, *[t for pair in segs for t in pair])
@@ -325,7 +340,7 @@ def fused_run(plan: Plan, segments, X: torch.Tensor, workspace: torch.Tensor | N
         if w.dtype != torch.bfloat16 or y.dtype != torch.float32:
             raise TypeError("segment W must be bfloat16 and Y float32")
         arr[i] = Segment(w.data_ptr(), w.shape[0], _row_stride(w, "W"), y.data_ptr(),
-                         _row_stride(y, "Y") if y.dim() == 2 else w.shape[0])
+                         _row_stride(y, "Y"))
     if X.dtype != torch.bfloat16:
         raise TypeError("X must be bfloat16")
     _on_gpu("gemv_fused_run", X, *[t for pair in segs for t in pair],
@@ -405,10 +420,12 @@ class Chain:
             for j, (w, y) in enumerate(segments):
                 if w.dtype != torch.bfloat16 or y.dtype != torch.float32:
                     raise TypeError("chain weights must be bfloat16 and outputs float32")
+                _vector(y, "chain Y")
                 segs[j] = Segment(w.data_ptr(), w.shape[0], _row_stride(w, "W"), y.data_ptr(),
                                   w.shape[0])
             if x.dtype != torch.bfloat16:
                 raise TypeError("chain inputs must be bfloat16")
+            _vector(x, "chain X")
             _on_gpu("gemv_chain_create", x, *[t for pair in segments for t in pair])
             for w, y in segments:
                 _need(w, w.shape[0], x.shape[-1], "chain W")

@@ -11,6 +11,7 @@ import re
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -80,17 +81,25 @@ def build(out: str = LIB_PATH, save_temps: str | None = None) -> str:
         plan_o = os.path.join(tmp, "plan.o")
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
         objs, remarks = [plan_o], []
-        for unit in HIP_UNITS:
+
+        def compile_unit(unit):
             obj = os.path.join(tmp, unit + ".o")
-            remarks += _run([HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage",
-                             "-c", os.path.join(CSRC, unit + ".hip"), "-o", obj])
-            objs.append(obj)
+            rem = _run([HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage",
+                        "-c", os.path.join(CSRC, unit + ".hip"), "-o", obj])
             if save_temps:
                 # the device assembly, for reading the generated code
                 os.makedirs(save_temps, exist_ok=True)
                 _run([HIPCC, *HIP_FLAGS, "--cuda-device-only", "-S",
                       os.path.join(CSRC, unit + ".hip"),
                       "-o", os.path.join(save_temps, f"{unit}-hip-amdgcn-amd-amdhsa-gfx950.s")])
+            return obj, rem
+
+        # one compiler process per translation unit, at most as many as the host's CPUs
+        workers = max(1, min(len(HIP_UNITS), len(os.sched_getaffinity(0)), 16))
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            for obj, rem in pool.map(compile_unit, HIP_UNITS):
+                objs.append(obj)
+                remarks += rem
         tmp_out = out + ".tmp"
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_out])
         kernels = _resources(remarks)

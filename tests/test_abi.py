@@ -267,3 +267,33 @@ def test_package_fails_loudly_without_the_library(tmp_path):
                           cwd=tmp_path, capture_output=True, text=True, timeout=300)
     assert proc.returncode != 0
     assert "ImportError" in proc.stderr and "no fallback" in proc.stderr, proc.stderr[-500:]
+
+
+def test_binding_refuses_strided_rows():
+    """A view whose elements along a row are not adjacent (buf[::2], M[:, j]) would be read
+    by the kernels as if it were dense; the binding refuses it, for 1-D and 2-D operands and
+    for the single-vector operands of the INT4, RMSNorm and chain calls."""
+    from bandwidth_bound_decode_amd import _binding as b
+
+    buf = torch.zeros(512, dtype=torch.bfloat16)
+    mat = torch.zeros((64, 256), dtype=torch.bfloat16)
+    assert buf[::2].stride() == (2,)
+    with pytest.raises(ValueError, match="contiguous"):
+        b._row_stride(buf[::2], "X")
+    with pytest.raises(ValueError, match="contiguous"):
+        b._row_stride(mat[:, 3], "X")
+    with pytest.raises(ValueError, match="contiguous"):
+        b._row_stride(mat[:, ::2], "W")
+    with pytest.raises(ValueError, match="contiguous"):
+        b._vector(buf[::2], "H")
+    with pytest.raises(ValueError, match=r"\[k\] or \[1, k\]"):
+        b._vector(mat[:2], "X")
+    # dense operands and one-element rows pass, with the row stride the kernels expect
+    assert b._row_stride(buf, "X") == 512
+    assert b._row_stride(buf[:1], "X") == 1
+    assert b._row_stride(mat, "W") == 256
+    assert b._row_stride(mat[:, :100], "W") == 256
+    assert b._row_stride(mat[:1, :100], "W") == 100
+    assert b._row_stride(mat[:, :1], "W") == 256
+    b._vector(mat[:1], "X")
+    b._vector(buf, "X")
