@@ -145,6 +145,50 @@ def time_graph(torch, launch, count: int, stream):
     return start.elapsed_time(end) / 1e3
 
 
+def time_windows(torch, launch, per_graph: int, windows: int, min_launches: int, stream):
+    """Per-launch time of `launch` run back to back, independent of the graph size.
+
+    The `per_graph` launches are captured into one graph on `stream`. Each of `windows`
+    windows replays it `reps` times back to back (enough replays for >= `min_launches`
+    launches), bracketed by HIP events on `stream`; the per-launch time of a window is its
+    span over reps * per_graph. Each window is followed by one single-replay window, whose
+    excess over per_graph launches is the replay's own overhead (graph submission and the
+    events), reported apart. Returns a dict of medians and the per-window figures."""
+    import bandwidth_bound_decode_amd as bbd
+    g = bbd.Graph(stream)
+    with torch.cuda.stream(stream):
+        with g:
+            for i in range(per_graph):
+                launch(i)
+    reps = max(1, math.ceil(min_launches / per_graph))
+    for _ in range(2):                       # untimed replays
+        g.launch(stream)
+    torch.cuda.synchronize()
+    per, single = [], []
+    for _ in range(windows):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        c = torch.cuda.Event(enable_timing=True)
+        d = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.launch(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        c.record(stream)                     # one replay from an idle stream, as a lone step
+        g.launch(stream)
+        d.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / 1e3 / (reps * per_graph))
+        single.append(c.elapsed_time(d) / 1e3)
+    g.destroy()
+    launch_s = statistics.median(per)
+    return {"launch_s": launch_s, "per_window_s": per, "windows": windows, "reps": reps,
+            "per_graph": per_graph, "timed_launches": windows * reps * per_graph,
+            "replay_overhead_s": statistics.median(single) - per_graph * launch_s,
+            "spread": (max(per) - min(per)) / launch_s}
+
+
 def rotation_arena(torch, w, min_bytes=ROTATION_BYTES):
     nbytes = w.numel() * w.element_size()
     copies = max(2, math.ceil(min_bytes / nbytes) + 1)
@@ -154,9 +198,11 @@ def rotation_arena(torch, w, min_bytes=ROTATION_BYTES):
     return arena
 
 
-def bench_gemv(torch, bbd, g, w, x, steps, warmup, segments=(), **plan_opts):
-    """Rotated timing of one GEMV shape (fused when `segments` is given): per-launch event
-    pairs, and the same launches back to back from one graph."""
+def bench_gemv(torch, bbd, g, w, x, steps, warmup, segments=(), windows=5, min_launches=200,
+               **plan_opts):
+    """Rotated timing of one GEMV shape (fused when `segments` is given): the launches back
+    to back from one graph over several windows (the figure reported), and isolated
+    launches each bracketed by its own events (these include the events' overhead)."""
     W = w.to("cuda")
     X = x.to("cuda")
     arena = rotation_arena(torch, W)
@@ -178,21 +224,25 @@ def bench_gemv(torch, bbd, g, w, x, steps, warmup, segments=(), **plan_opts):
     else:
         def launch(i, stream=None):
             bbd.run(plan, arena[i % copies], X, Y, ws, stream)
-    # per-launch durations: every launch bracketed by its own events (host-paced)
+    # isolated launches: every launch bracketed by its own events (host-paced; the figure
+    # includes the events' own ~2 us, so it is context, not the bandwidth figure)
     _, per = time_launches(torch, launch, steps, warmup, stream)
     # back to back: the same rotated launches replayed from one graph on a side stream
     side = torch.cuda.Stream()
-    total = time_graph(torch, lambda i: launch(i, side), steps, side)
+    tw = time_windows(torch, lambda i: launch(i, side), steps, windows, min_launches, side)
     nb = alg_bytes(g.n, g.k, g.m)
+    t = tw["launch_s"]
     res = {"shape": f"{g.n}x{g.k}", "m": g.m, "plan": plan.info, "alg_bytes": nb,
-           "rotation_copies": copies, "us_median": statistics.median(per) * 1e6,
-           "us_p10": pct(per, 0.1) * 1e6, "us_p90": pct(per, 0.9) * 1e6,
-           "us_mean": statistics.fmean(per) * 1e6, "us_per_step_back_to_back": total / steps * 1e6,
-           "TBps_median": nb / statistics.median(per) / 1e12,
-           "TBps_back_to_back": nb * steps / total / 1e12}
-    res["pct_peak_median"] = 100 * res["TBps_median"] * 1e12 / PEAK_HBM
+           "rotation_copies": copies,
+           "us_per_launch": t * 1e6, "TBps": nb / t / 1e12, "pct_peak": 100 * nb / t / PEAK_HBM,
+           "windows": tw["windows"], "launches_per_window": tw["reps"] * tw["per_graph"],
+           "window_spread": tw["spread"],
+           "replay_overhead_us": tw["replay_overhead_s"] * 1e6,
+           "isolated_launch_us_median": statistics.median(per) * 1e6,
+           "isolated_launch_us_p10": pct(per, 0.1) * 1e6,
+           "isolated_launch_us_p90": pct(per, 0.9) * 1e6}
     del arena
-    return res, total, per, plan
+    return res, tw, per, plan
 
 
 def bench_int4(torch, bbd, workloads, name, n, k, steps, warmup):
@@ -216,17 +266,16 @@ def bench_int4(torch, bbd, workloads, name, n, k, steps, warmup):
         bbd.run_int4(plan, wa[i % copies], sa[i % copies], x, Y, stream)
     _, per = time_launches(torch, launch, steps, warmup, stream)
     side = torch.cuda.Stream()
-    total = time_graph(torch, lambda i: launch(i, side), steps, side)
+    tw = time_windows(torch, lambda i: launch(i, side), steps, 5, 200, side)
+    t = tw["launch_s"]
     nb = unit + 2 * k + 4 * n
     info = plan.info
     res = {"name": name, "weights": "int4", "shape": f"{n}x{k}", "m": 1, "alg_bytes": nb,
            "plan": {key: info[key] for key in ("rows_per_wave", "unroll", "waves_per_block",
                                                "grid_x", "lds_bytes")},
-           "rotation_copies": copies, "us_median": statistics.median(per) * 1e6,
-           "us_per_step_back_to_back": total / steps * 1e6,
-           "TBps_median": nb / statistics.median(per) / 1e12,
-           "TBps_back_to_back": nb * steps / total / 1e12}
-    res["pct_peak_back_to_back"] = 100 * res["TBps_back_to_back"] * 1e12 / PEAK_HBM
+           "rotation_copies": copies, "us_per_launch": t * 1e6, "TBps": nb / t / 1e12,
+           "pct_peak": 100 * nb / t / PEAK_HBM, "window_spread": tw["spread"],
+           "isolated_launch_us_median": statistics.median(per) * 1e6}
     del wa, sa
     return res
 
@@ -267,8 +316,8 @@ def bench_rmsnorm(torch, bbd, workloads, name, segments, k, steps):
             bbd.fused_run(plain_plan, [(wi[a:b], yy) for (a, b), yy in
                                        zip(zip(bounds[:-1], bounds[1:]), ys2)], x, None, stream)
     side = torch.cuda.Stream()
-    t_fused = time_graph(torch, lambda i: fused(i, side), steps, side) / steps
-    t_plain = time_graph(torch, lambda i: plain(i, side), steps, side) / steps
+    t_fused = time_windows(torch, lambda i: fused(i, side), steps, 5, 200, side)["launch_s"]
+    t_plain = time_windows(torch, lambda i: plain(i, side), steps, 5, 200, side)["launch_s"]
     # the norm as its own launch, eagerly back to back (torch's kernel; not on the GEMV path)
     for _ in range(10):
         torch.nn.functional.rms_norm(h.float(), (k,), gain.float(), 1e-5)
@@ -434,6 +483,68 @@ def cpu_baseline(w, x, runs=3):
     return t, threads
 
 
+def oracle_per_config(workloads, runs=3):
+    """The oracle on every workload, on 1 thread and on all host threads: 1 untimed run then
+    the median of `runs`. The decode step is sampled as one layer (QKV, o_proj, gate_up, down)
+    plus lm_head and scaled to 32 layers + lm_head; its inputs are drawn on the host with the
+    step's shapes and distributions."""
+    import numpy as np
+    import oracle
+    import torch
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def timed(wb, xb, threads):
+        oracle.gemv(wb, xb, nthreads=threads)
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            oracle.gemv(wb, xb, nthreads=threads)
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    all_threads = oracle.threads(0)
+    rows = []
+
+    def add(name, gemvs, scale=None, sample=None):
+        entry = {"config": name, "gemvs": [f"{g.name} {g.n}x{g.k} m={g.m}" for g, _, _ in gemvs]}
+        nbytes = sum(alg_bytes(g.n, g.k, g.m) for g, _, _ in gemvs)
+        for label, th in (("1_thread", 1), ("all_threads", all_threads)):
+            per = [timed(wb, xb, th) for _, wb, xb in gemvs]
+            t = sum(per) if scale is None else scale(per)
+            entry[f"seconds_{label}"] = round(t, 5)
+            entry[f"GBps_{label}"] = round((nbytes if scale is None else scale_bytes) / t / 1e9, 4)
+        entry["threads_all"] = all_threads
+        if sample:
+            entry["sample"] = sample
+        rows.append(entry)
+        log(f"oracle {name}: {entry['seconds_1_thread'] * 1e3:.1f} ms on 1 thread, "
+            f"{entry['seconds_all_threads'] * 1e3:.1f} ms on {all_threads}")
+
+    def drawn(cfg):
+        return [(g, bits(w), bits(x)) for g, (w, x) in zip(cfg.gemvs, workloads.draw_config(cfg))]
+
+    scale_bytes = None
+    add("k_proj_and_tails", drawn(workloads.K_PROJ_AND_TAILS))
+    add("down_proj", drawn(workloads.DOWN_PROJ))
+    add("fused_projections", drawn(workloads.FUSED_PROJECTIONS))
+    add("skinny_batch", drawn(workloads.SKINNY_BATCH))
+    layer = [g for g in workloads.decode_step_gemvs()[:4]] + [workloads.decode_step_gemvs()[-1]]
+    gen = workloads.generator(6000)
+    sample = []
+    for g in layer:
+        w = workloads.bf16_normal((g.n, g.k), workloads.SIGMA_W, gen)
+        x = workloads.bf16_normal((g.m, g.k), workloads.SIGMA_X, gen)
+        sample.append((g, bits(w), bits(x)))
+    layers = workloads.LAYERS
+    scale_bytes = sum(alg_bytes(g.n, g.k, g.m) for g in workloads.decode_step_gemvs())
+    add("decode_step", sample, scale=lambda per: layers * sum(per[:4]) + per[4],
+        sample=f"one layer (QKV, o_proj, gate_up, down) and lm_head timed, scaled to "
+               f"{layers} layers + lm_head")
+    return rows
+
+
 # ---------------------------------------------------------------------------- main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -442,10 +553,15 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-replays", type=int, default=20)
     ap.add_argument("--shape-steps", type=int, default=100)
+    ap.add_argument("--windows", type=int, default=7,
+                    help="timing windows for the headline (median reported, at least 5)")
+    ap.add_argument("--window-launches", type=int, default=200,
+                    help="back-to-back launches per timing window (at least)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-shapes", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     args = ap.parse_args(argv)
+    args.windows = max(5, args.windows)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this GEMV build has no multi-GPU path "
@@ -469,14 +585,17 @@ def main(argv=None):
     cfg = workloads.DOWN_PROJ
     g = cfg.gemvs[0]
     (w, x), = workloads.draw_config(cfg)
-    res, total, per, plan = bench_gemv(torch, bbd, g, w, x, args.steps, args.warmup)
+    res, tw, per, plan = bench_gemv(torch, bbd, g, w, x, args.steps, args.warmup,
+                                    windows=args.windows, min_launches=args.window_launches)
     nb = res["alg_bytes"]
-    value_TBps = nb * args.steps / total / 1e12
-    mean_launch = total / args.steps          # back to back, from one graph replay
-    achieved_GBps = nb / mean_launch / 1e9
-    log(f"down 4096x14336: {res['us_median']:.2f} us median per launch, "
-        f"{res['TBps_median']:.3f} TB/s; {value_TBps:.3f} TB/s back to back over "
-        f"{args.steps} graph-replayed launches; plan {plan.info}")
+    launch_s = tw["launch_s"]                 # median over the windows, back to back
+    value_TBps = nb / launch_s / 1e12
+    achieved_GBps = nb / launch_s / 1e9
+    log(f"down 4096x14336: {launch_s * 1e6:.3f} us per launch back to back (median of "
+        f"{tw['windows']} windows of {tw['reps'] * tw['per_graph']} launches, spread "
+        f"{100 * tw['spread']:.2f} %), {value_TBps:.3f} TB/s; replay overhead "
+        f"{tw['replay_overhead_s'] * 1e6:.1f} us; isolated launches "
+        f"{res['isolated_launch_us_median']:.2f} us; plan {plan.info}")
     traffic, traffic_note = counter_traffic(plan.info)
 
     out = {
@@ -486,7 +605,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(total / args.steps * 1e3, 6),
+        "ms_per_step": round(launch_s * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -497,18 +616,32 @@ def main(argv=None):
                    "n": g.n, "k": g.k, "m": g.m, "sigma_w": workloads.SIGMA_W,
                    "sigma_x": workloads.SIGMA_X, "seed": cfg.seed,
                    "rotation_copies": res["rotation_copies"], "plan": plan.info},
+        "timing": {"method": "the K steps (one rotated launch each) captured in one graph; "
+                             "each window replays it back to back enough times for "
+                             f">= {args.window_launches} launches between two HIP events on "
+                             "the replay stream; value and ms_per_step use the median window",
+                   "windows": tw["windows"], "launches_per_window": tw["reps"] * tw["per_graph"],
+                   "timed_launches": tw["timed_launches"],
+                   "per_window_us": [round(t * 1e6, 4) for t in tw["per_window_s"]],
+                   "window_spread": round(tw["spread"], 5),
+                   "replay_overhead_us": round(tw["replay_overhead_s"] * 1e6, 3),
+                   "replay_overhead_note": "one replay of the K-launch graph from an idle "
+                                           "stream minus K back-to-back launches: graph "
+                                           "submission and event cost, paid once per replay"},
         "pct_of_peak": round(100 * value_TBps * 1e12 / PEAK_HBM, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved_GBps, 1), "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": round(achieved_GBps * 1e9 / PEAK_HBM, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
                      "alg_bytes_per_launch": nb,
-                     "launch_us_mean": round(mean_launch * 1e6, 3),
-                     "timing": "mean launch duration over the timed region: K rotated launches "
-                               "replayed back to back from one graph, bracketed by HIP events "
-                               "on the replay stream",
-                     "isolated_launch_us_median": round(res["us_median"], 3),
-                     "isolated_launch_us_p10": round(res["us_p10"], 3),
-                     "isolated_launch_us_p90": round(res["us_p90"], 3)},
+                     "launch_us_mean": round(launch_s * 1e6, 3),
+                     "timing": "mean launch duration back to back: median over the windows "
+                               "of (window span / launches in it), HIP events on the replay "
+                               "stream",
+                     "isolated_launch_us_median": round(res["isolated_launch_us_median"], 3),
+                     "isolated_launch_us_p10": round(res["isolated_launch_us_p10"], 3),
+                     "isolated_launch_us_p90": round(res["isolated_launch_us_p90"], 3),
+                     "isolated_note": "each launch bracketed by its own events, host-paced; "
+                                      "includes the events' cost"},
         "device": {"name": props.name, "arch": arch, "cus": props.multi_processor_count,
                    "peak_hbm_TBps_assumed": PEAK_HBM / 1e12},
         "h100_context": H100,
@@ -523,6 +656,7 @@ def main(argv=None):
                                "seconds_per_gemv": round(t_cpu, 4),
                                "host_cpus": len(os.sched_getaffinity(0))}
         log(f"cpu oracle: {t_cpu * 1e3:.1f} ms per GEMV on {threads} threads")
+        out["cpu_baseline"]["per_config"] = oracle_per_config(workloads)
 
     if not args.skip_shapes:
         shapes = []
@@ -538,8 +672,15 @@ def main(argv=None):
                        ()))
         for gg, (ww, xx) in zip(workloads.SKINNY_BATCH.gemvs, workloads.draw_config(workloads.SKINNY_BATCH)):
             shapes.append((gg.name, gg, ww, xx, ()))
+        # the unaligned 4097 x 14337 tail at the batches where x no longer fits in LDS whole
+        for m in (8, 16):
+            gt = workloads.Gemv(f"skinny_tail_m{m}", workloads.HIDDEN + 1,
+                                workloads.INTERMEDIATE + 1, m)
+            shapes.append((gt.name, gt, *workloads.draw_gemv(gt, workloads.generator(90 + m)),
+                           ()))
         for name, gg, ww, xx, segs in shapes:
-            r, _, _, _ = bench_gemv(torch, bbd, gg, ww, xx, args.shape_steps, 10, segs)
+            r, _, _, _ = bench_gemv(torch, bbd, gg, ww, xx, args.shape_steps, 10, segs,
+                                    windows=5, min_launches=args.window_launches)
             r["name"] = name
             info = r["plan"]
             r["plan"] = {k: info[k] for k in ("splits", "rows_per_wave", "unroll",
@@ -551,7 +692,8 @@ def main(argv=None):
             for k in list(r):
                 if isinstance(r[k], float):
                     r[k] = round(r[k], 3)
-            log(f"{name}: {r['us_median']:.2f} us, {r['TBps_median']:.3f} TB/s")
+            log(f"{name}: {r['us_per_launch']:.2f} us back to back, {r['TBps']:.3f} TB/s "
+                f"({r['pct_peak']:.1f} %)")
             out.setdefault("shapes", []).append(r)
         # the RMSNorm prologue fused into the projections that consume the normalised x
         for name, segs in (("rmsnorm_qkv", (4096, 1024, 1024)), ("rmsnorm_gate_up", (14336, 14336))):
@@ -571,8 +713,8 @@ def main(argv=None):
             for key in list(r):
                 if isinstance(r[key], float):
                     r[key] = round(r[key], 3)
-            log(f"{name}: {r['us_per_step_back_to_back']:.2f} us back to back, "
-                f"{r['TBps_back_to_back']:.3f} TB/s")
+            log(f"{name}: {r['us_per_launch']:.2f} us back to back, {r['TBps']:.3f} TB/s "
+                f"({r['pct_peak']:.1f} %)")
             out.setdefault("int4_shapes", []).append(r)
 
     if not args.skip_decode:

@@ -7,7 +7,7 @@ import torch
 
 import bandwidth_bound_decode_amd as bbd
 import workloads
-from gpu_helpers import (bits_equal, device_matrix, draw, gemv, host_bits, oracle_check,
+from gpu_helpers import (DEV, bits_equal, device_matrix, draw, gemv, host_bits, oracle_check,
                          output)
 
 pytestmark = pytest.mark.gpu
@@ -47,6 +47,24 @@ def test_down_proj_full_size():
     Y, p = gemv(W, X)
     oracle_check(W, X, Y, "down 4096x14336")
     Y2, _ = gemv(W, X, plan=p)
+    assert bits_equal(Y, Y2), "two runs of one plan differ"
+
+
+@pytest.mark.parametrize("name,n,k,unroll", [("o_proj", 4096, 4096, 4),
+                                              ("lm_head", workloads.VOCAB, workloads.HIDDEN, 8)])
+def test_single_matrix_decode_shapes_full_size(name, n, k, unroll):
+    """The single-matrix K = 4096 decode shapes at full size, every output against the
+    oracle: o_proj 4096x4096 and the 128256-row lm_head (the only single-matrix user of the
+    one-burst-per-row tile), in the plans the bench and the decode step use."""
+    g = workloads.Gemv(name, n, k)
+    w, x = workloads.draw_gemv(g, workloads.generator(8 if name == "lm_head" else 7, DEV), DEV)
+    p = bbd.Plan(n, k, 1)
+    info = p.info
+    assert (info["splits"], info["rows_per_wave"], info["unroll"]) == (1, 1, unroll), info
+    Y, _ = gemv(w, x, plan=p)
+    rep = oracle_check(w, x, Y, f"{name} {n}x{k}")
+    print(f"{name} {n}x{k}: {rep}", flush=True)
+    Y2, _ = gemv(w, x, plan=p)
     assert bits_equal(Y, Y2), "two runs of one plan differ"
 
 

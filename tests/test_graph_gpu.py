@@ -1,5 +1,5 @@
 """GPU parity of the graph-captured decode step: every replay bitwise equal to the eager
-sequence, and sampled outputs of all 129 GEMVs within tolerance of the oracle."""
+sequence, and every output of all 129 GEMVs within tolerance of the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -79,20 +79,23 @@ def test_decode_step_full():
         for i, (a, b) in enumerate(zip(snapshot(seq), eager)):
             assert bits_equal(a, b), f"chain run {rep}: call {i} differs from eager"
     chain.destroy()
-    rng = np.random.default_rng(4)
+    # Every output of every GEMV against the oracle, one weight matrix on the host at a time
+    # (at most the 1 GB lm_head).
+    worst = 0.0
     for i, ((g, parts, x), y) in enumerate(zip(drawn, eager)):
-        n = g.n
-        rows = np.unique(np.concatenate([[0, 1, n // 2, n - 1], rng.integers(0, n, 12)]))
-        bounds = np.cumsum([0] + [p.shape[0] for p in parts])
-        sel = []
-        for r in rows:
-            j = int(np.searchsorted(bounds, r, side="right") - 1)
-            sel.append(parts[j][r - bounds[j]])
-        w_rows = torch.stack(sel)
-        y_ref, s_abs = oracle.gemv(host_bits(w_rows), host_bits(x))
-        got = y.cpu().numpy()[:, rows]
-        rep = oracle.check(got, y_ref, s_abs)
-        assert rep.ok, f"{g.name}: {rep}"
+        xb = host_bits(x)
+        y_host = y.cpu().numpy()
+        col = 0
+        for j, part in enumerate(parts):
+            n = part.shape[0]
+            y_ref, s_abs = oracle.gemv(host_bits(part), xb)
+            rep = oracle.check(y_host[:, col:col + n], y_ref, s_abs)
+            assert rep.ok, f"call {i} ({g.name}) segment {j}: {rep}"
+            worst = max(worst, rep.worst_ratio)
+            col += n
+        assert col == y_host.shape[1]
+    print(f"decode step: all {sum(c.n for c in seq.calls)} outputs within tolerance, "
+          f"worst error / allowance {worst:.3g}", flush=True)
 
 
 def test_unaligned_and_matrix_core_calls_in_graph():
