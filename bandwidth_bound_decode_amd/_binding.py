@@ -92,6 +92,7 @@ SIGNATURES = {
     "gemv_plan_query": (_INT, [_P, ctypes.POINTER(PlanInfo)]),
     "gemv_plan_destroy": (None, [_P]),
     "gemv_run": (_INT, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _SZ, _P]),
+    "gemv_run_static": (_INT, [_P, _P, _I64, _P, _I64, _P, _I64, _P]),
     "gemv_fused_run": (_INT, [_P, ctypes.POINTER(Segment), _INT, _P, _I64, _P, _SZ, _P]),
     "gemv_int4_run": (_INT, [_P, _P, _I64, _P, _I64, _P, _P, _P]),
     "gemv_rmsnorm_run": (_INT, [_P, ctypes.POINTER(Segment), _INT, _P, _P, ctypes.c_float, _P]),
@@ -277,6 +278,25 @@ def run(plan: Plan, W: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
                        _row_stride(X, "X"), Y.data_ptr(), _row_stride(Y, "Y"), ws_ptr,
                        ws_bytes, _stream_handle(stream))
     _check(st, "gemv_run")
+    return Y
+
+
+def run_static(plan: Plan, W: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
+               stream=None) -> torch.Tensor:
+    """run() without a workspace: split partial sums go to the library's static per-GPU
+    scratch (gemv_run_static). Calls that overlap on one GPU race. Returns Y."""
+    if W.dtype != torch.bfloat16 or X.dtype != torch.bfloat16 or Y.dtype != torch.float32:
+        raise TypeError("W and X must be bfloat16 and Y float32")
+    _on_gpu("gemv_run_static", W, X, Y)
+    if W.dim() != 2 or W.shape[0] != plan.n:
+        raise ValueError(f"W is {tuple(W.shape)}, the plan has {plan.n} rows")
+    _need(W, plan.n, plan.k, "W")
+    _need(X, plan.m, plan.k, "X")
+    _need(Y, plan.m, plan.n, "Y")
+    st = _lib.gemv_run_static(plan.handle, W.data_ptr(), _row_stride(W, "W"), X.data_ptr(),
+                              _row_stride(X, "X"), Y.data_ptr(), _row_stride(Y, "Y"),
+                              _stream_handle(stream))
+    _check(st, "gemv_run_static")
     return Y
 
 

@@ -33,6 +33,7 @@
 
 #include <array>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -868,9 +869,10 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 bool aligned2(const void *p) { return ((uintptr_t)p & 1u) == 0; }
 
-// Validation shared by gemv_run and gemv_fused_run; makes no HIP call.
-gemv_status validate(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
-                     int64_t ldx, void *ws, size_t ws_bytes)
+// Validation of everything but the workspace, shared by gemv_run, gemv_fused_run and
+// gemv_run_static; makes no HIP call.
+gemv_status validate_call(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
+                          int64_t ldx)
 {
     if (!p || !segs || nseg < 1 || nseg > GEMV_MAX_SEGMENTS || !X ||
         p->weights != GEMV_WEIGHTS_BF16 || p->prologue != 0)
@@ -894,6 +896,16 @@ gemv_status validate(gemv_plan_t p, const gemv_segment *segs, int nseg, const vo
     for (int i = 0; i < nseg; ++i)
         if (!aligned2(segs[i].W) || !aligned4(segs[i].Y))
             return GEMV_ERR_MISALIGNED;
+    return GEMV_OK;
+}
+
+// Validation shared by gemv_run and gemv_fused_run (caller's workspace); no HIP call.
+gemv_status validate(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
+                     int64_t ldx, void *ws, size_t ws_bytes)
+{
+    gemv_status st = validate_call(p, segs, nseg, X, ldx);
+    if (st != GEMV_OK)
+        return st;
     if (p->workspace) {
         if (!ws || ws_bytes < p->workspace)
             return GEMV_ERR_WORKSPACE;
@@ -903,13 +915,12 @@ gemv_status validate(gemv_plan_t p, const gemv_segment *segs, int nseg, const vo
     return GEMV_OK;
 }
 
-gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
-                   int64_t ldx, void *ws, size_t ws_bytes, void *stream)
+// Launch a validated call. A split launch (VALU or matrix-core) takes its arrival tickets
+// and partial sums from `tickets` and `partials`; an unsplit one touches neither.
+gemv_status launch_on(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
+                      int64_t ldx, unsigned *tickets, float *partials, void *stream)
 {
-    gemv_status st = validate(p, segs, nseg, X, ldx, ws, ws_bytes);
-    if (st != GEMV_OK)
-        return st;
-
+    gemv_status st;
     bool fast = aligned16(X) && (p->m == 1 || ldx % 8 == 0);
     for (int i = 0; i < nseg; ++i)
         fast = fast && aligned16(segs[i].W) && segs[i].ldw % 8 == 0;
@@ -918,7 +929,7 @@ gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void
     st = bbd::launch_whole(p, segs, nseg, X, stream, &done);
     if (done || st != GEMV_OK)
         return st;
-    st = bbd::launch_mfma(p, segs, nseg, X, ldx, ws, stream, &done);
+    st = bbd::launch_mfma(p, segs, nseg, X, ldx, tickets, partials, stream, &done);
     if (done || st != GEMV_OK)
         return st;
     st = bbd::launch_batch(p, segs, nseg, X, ldx, stream, &done);
@@ -943,10 +954,8 @@ gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void
     a.slice = (int32_t)p->slice;
     a.waves = p->waves_per_block;
     a.rows = p->rows_per_wave;
-    a.tickets = p->splits > 1 ? static_cast<unsigned *>(ws) : nullptr;
-    a.partial = p->splits > 1
-                    ? reinterpret_cast<float *>(static_cast<char *>(ws) + p->partial_offset)
-                    : nullptr;
+    a.tickets = p->splits > 1 ? tickets : nullptr;
+    a.partial = p->splits > 1 ? partials : nullptr;
     const bool multi = nseg > 1;
     if (multi) {
         int64_t row0 = 0;
@@ -978,6 +987,22 @@ gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void
     if (e != hipSuccess)
         return device_error(e);
     return GEMV_OK;
+}
+
+// gemv_run / gemv_fused_run: the caller's workspace holds the tickets, then the partials.
+gemv_status launch(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
+                   int64_t ldx, void *ws, size_t ws_bytes, void *stream)
+{
+    gemv_status st = validate(p, segs, nseg, X, ldx, ws, ws_bytes);
+    if (st != GEMV_OK)
+        return st;
+    unsigned *tickets = nullptr;
+    float *partials = nullptr;
+    if (p->workspace) {
+        tickets = static_cast<unsigned *>(ws);
+        partials = reinterpret_cast<float *>(static_cast<char *>(ws) + p->partial_offset);
+    }
+    return launch_on(p, segs, nseg, X, ldx, tickets, partials, stream);
 }
 
 // The plan's LDS reservation assumes an allocation unit; confirm with the runtime's
@@ -1021,6 +1046,112 @@ gemv_status fit_cap(gemv_plan_t p, int device)
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------------------
+// Scratch for gemv_run_static: the split launches' arrival tickets (the first
+// GEMV_STATIC_TICKET_SLOTS words) and partial sums (the rest), one copy per GPU, held until
+// the process ends. Host code never uses this name as an address (on the host it is only a
+// stand-in for the device symbol): the per-device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[GEMV_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kStaticMaxDevices = 64;
+constexpr size_t kStaticTicketBytes = (size_t)GEMV_STATIC_TICKET_SLOTS * sizeof(unsigned);
+static_assert(kStaticTicketBytes % 256 == 0, "partial sums start 256-byte aligned");
+static_assert(GEMV_STATIC_SCRATCH_BYTES > kStaticTicketBytes, "room for partial sums");
+
+std::mutex g_scratch_mutex;                                   // serialises the set-up
+std::atomic<char *> g_scratch_ptr[kStaticMaxDevices];         // device address, per device
+
+__global__ void __launch_bounds__(256) clear_words(unsigned *p, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
+// The device address of `scratch` on `device`, looked up once per device with that device
+// current. The first look-up also enqueues, on `stream`, a kernel that zeroes the ticket
+// region (a fill kernel rather than a memset, so a capture that records it holds no memset
+// node); every completed split call leaves its tickets at zero again.
+gemv_status static_scratch(int device, void *stream, char **out)
+{
+    *out = nullptr;
+    if (device < 0 || device >= kStaticMaxDevices)
+        return record_hip_error(0, GEMV_ERR_DEVICE);
+    char *ptr = g_scratch_ptr[device].load(std::memory_order_acquire);
+    if (ptr) {
+        *out = ptr;
+        return GEMV_OK;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ptr = g_scratch_ptr[device].load(std::memory_order_acquire);
+    if (ptr) {
+        *out = ptr;
+        return GEMV_OK;
+    }
+    int prev = 0;
+    hipError_t e = hipGetDevice(&prev);
+    if (e == hipSuccess && prev != device)
+        e = hipSetDevice(device);
+    void *addr = nullptr;
+    if (e == hipSuccess)
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e == hipSuccess) {
+        unsigned *tickets = static_cast<unsigned *>(addr);
+        int words = GEMV_STATIC_TICKET_SLOTS;
+        void *args[] = {&tickets, &words};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(clear_words),
+                            dim3((unsigned)(GEMV_STATIC_TICKET_SLOTS / 256)), dim3(256), args, 0,
+                            static_cast<hipStream_t>(stream));
+    }
+    if (prev != device)
+        (void)hipSetDevice(prev);
+    if (e != hipSuccess)
+        return device_error(e);
+    ptr = static_cast<char *>(addr);
+    g_scratch_ptr[device].store(ptr, std::memory_order_release);
+    *out = ptr;
+    return GEMV_OK;
+}
+
+}  // namespace
+
+extern "C" gemv_status gemv_run_static(gemv_plan_t p, const void *W, int64_t ldw, const void *X,
+                                       int64_t ldx, float *Y, int64_t ldy, void *stream)
+{
+    if (!p)
+        return GEMV_ERR_INVALID_ARG;
+    gemv_segment seg = {W, p->n, ldw, Y, ldy};
+    gemv_status st = validate_call(p, &seg, 1, X, ldx);
+    if (st != GEMV_OK)
+        return st;
+    if (!p->workspace)                      // unsplit: no scratch at all
+        return launch_on(p, &seg, 1, X, ldx, nullptr, nullptr, stream);
+    // The launch that splits (VALU, matrix-core or both) must fit the static layout.
+    int64_t blocks = 0;
+    if (p->splits > 1)
+        blocks = p->grid_x;
+    if (p->mfma && p->mfma_splits > 1 && p->mfma_grid_x > blocks)
+        blocks = p->mfma_grid_x;
+    const size_t partial_bytes = p->workspace - p->partial_offset;
+    if (blocks > GEMV_STATIC_TICKET_SLOTS ||
+        partial_bytes > (size_t)GEMV_STATIC_SCRATCH_BYTES - kStaticTicketBytes)
+        return GEMV_ERR_WORKSPACE;
+    int device = p->device;
+    if (device < 0) {
+        hipError_t e = hipGetDevice(&device);
+        if (e != hipSuccess)
+            return device_error(e);
+    }
+    char *base = nullptr;
+    st = static_scratch(device, stream, &base);
+    if (st != GEMV_OK)
+        return st;
+    return launch_on(p, &seg, 1, X, ldx, reinterpret_cast<unsigned *>(base),
+                     reinterpret_cast<float *>(base + kStaticTicketBytes), stream);
+}
 
 struct gemv_graph_s {
     hipGraph_t graph;

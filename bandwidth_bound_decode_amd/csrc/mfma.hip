@@ -165,7 +165,8 @@ __global__ void __launch_bounds__(kThreads)
 namespace bbd {
 
 gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
-                        int64_t ldx, void *ws, void *stream, bool *done)
+                        int64_t ldx, unsigned *ws_tickets, float *ws_partial, void *stream,
+                        bool *done)
 {
     *done = false;
     if (!p->mfma || nseg != 1 || ((uintptr_t)X & 15u) || ldx % 8 != 0 ||
@@ -178,8 +179,8 @@ gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const
     float *partial = nullptr;
     unsigned *tickets = nullptr;
     if (p->mfma_splits > 1) {
-        tickets = static_cast<unsigned *>(ws);
-        partial = reinterpret_cast<float *>(static_cast<char *>(ws) + p->partial_offset);
+        tickets = ws_tickets;
+        partial = ws_partial;
     }
     int n = (int)p->n, k = (int)p->k, ldw = (int)segs[0].ldw, ldxi = (int)ldx,
         ldy = (int)segs[0].ldy, m = p->m, slice = (int)p->mfma_slice;

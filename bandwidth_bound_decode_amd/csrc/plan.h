@@ -82,9 +82,11 @@ gemv_status launch_batch(gemv_plan_t p, const gemv_segment *segs, int nseg, cons
                          int64_t ldx, void *stream, bool *done);
 
 // Launch a validated call on the matrix-core kernel (mfma.hip) when the plan chose it and
-// the call qualifies; *done tells whether it did.
+// the call qualifies; *done tells whether it did. A split launch takes its arrival tickets
+// and partial sums from `tickets` and `partial` (see the workspace layout in gemv.h).
 gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *X,
-                        int64_t ldx, void *ws, void *stream, bool *done);
+                        int64_t ldx, unsigned *tickets, float *partial, void *stream,
+                        bool *done);
 
 // RMSNorm-prologue launch (norm.hip) of a validated call; the plan's unroll picks the kernel.
 gemv_status launch_rmsnorm(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *H,

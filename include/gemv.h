@@ -197,6 +197,33 @@ gemv_status gemv_run(gemv_plan_t p,
                      void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * gemv_run with no workspace argument, for callers that cannot allocate device memory:
+ * code being captured into a graph, tight serving loops, harnesses that forbid hipMalloc.
+ * The split launches' arrival tickets and partial sums live in a static device array
+ * inside the library, GEMV_STATIC_SCRATCH_BYTES per GPU (held on every GPU the library
+ * runs on until the process ends): the first GEMV_STATIC_TICKET_SLOTS 32-bit words are
+ * tickets, the rest fp32 partial sums. Arguments, validation and the result are those of
+ * gemv_run; with the same plan and inputs the result is bitwise equal to gemv_run's.
+ *   - A plan that splits (the VALU or the matrix-core launch) and needs more than
+ *     GEMV_STATIC_TICKET_SLOTS row blocks, or more partial-sum bytes than the array holds
+ *     after the tickets, is refused with GEMV_ERR_WORKSPACE before any HIP call. Unsplit
+ *     plans use no scratch.
+ *   - Every call on a GPU shares that GPU's array and it keeps the last call's contents:
+ *     calls that overlap on one GPU (other streams, other threads) race and give wrong
+ *     results. Calls issued in order on one stream never overlap.
+ *   - The first call on a device looks the array up (hipGetSymbolAddress, on the plan's
+ *     device) and enqueues on `stream` one small kernel that zeroes the tickets; every
+ *     completed call leaves them at zero. No call allocates or synchronises with the host.
+ */
+#define GEMV_STATIC_SCRATCH_BYTES (4u << 20)
+#define GEMV_STATIC_TICKET_SLOTS 16384
+
+gemv_status gemv_run_static(gemv_plan_t p,
+                            const void *W, int64_t ldw,
+                            const void *X, int64_t ldx,
+                            float *Y, int64_t ldy, void *stream);
+
+/*
  * One GEMV over several weight matrices that share X: the fused QKV and gate_up
  * projections (decode-GEMV page, "A strong answer", cause 3). Segment i holds rows
  * [sum_{j<i} n_j, sum_{j<=i} n_j) of the plan's N rows:

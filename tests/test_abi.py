@@ -297,3 +297,30 @@ def test_binding_refuses_strided_rows():
     assert b._row_stride(mat[:, :1], "W") == 256
     b._vector(mat[:1], "X")
     b._vector(buf, "X")
+
+
+def test_static_entry_point_refuses_before_any_hip_call():
+    """gemv_run_static validates like gemv_run and refuses a split plan whose partial sums
+    exceed the static scratch array, all before any HIP call (host-only plans, fake
+    pointers)."""
+    lib = bbd.lib()
+    desc = DeviceDesc(256, 8.0e12, 1.0e-6)
+    h = ctypes.c_void_p()
+    # 2 slices x 16 vectors x 40000 rows x 4 B = 5.1 MB of partial sums > 4 MiB
+    opts = PlanOpts(2, 0, 0, 0, 0, -1, 0, 0)
+    assert lib.gemv_plan_for(ctypes.byref(h), 40000, 14336, 16, ctypes.byref(desc),
+                             ctypes.byref(opts)) == Status.OK
+    try:
+        assert lib.gemv_workspace_size(h) > 4 << 20
+        assert lib.gemv_run_static(h, FAKE, 14336, FAKE, 14336, FAKE, 40000,
+                                   None) == Status.WORKSPACE
+        assert lib.gemv_run_static(h, None, 14336, FAKE, 14336, FAKE, 40000,
+                                   None) == Status.INVALID_ARG
+        assert lib.gemv_run_static(h, FAKE, 14335, FAKE, 14336, FAKE, 40000,
+                                   None) == Status.INVALID_ARG
+        assert lib.gemv_run_static(h, FAKE + 1, 14336, FAKE, 14336, FAKE, 40000,
+                                   None) == Status.MISALIGNED
+    finally:
+        lib.gemv_plan_destroy(h)
+    assert lib.gemv_run_static(None, FAKE, 4096, FAKE, 4096, FAKE, 64, None) == \
+        Status.INVALID_ARG
