@@ -43,7 +43,8 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
                 ("waves_per_block", ctypes.c_int), ("unroll", ctypes.c_int),
                 ("waves_per_cu", ctypes.c_int), ("mfma", ctypes.c_int),
-                ("weights", ctypes.c_int), ("prologue", ctypes.c_int)]
+                ("weights", ctypes.c_int), ("prologue", ctypes.c_int),
+                ("int4_fp16", ctypes.c_int)]
 
 
 class DeviceDesc(ctypes.Structure):
@@ -61,7 +62,8 @@ class PlanInfo(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int), ("mfma", ctypes.c_int),
                 ("mfma_splits", ctypes.c_int), ("mfma_slice", ctypes.c_int64),
                 ("mfma_grid_x", ctypes.c_int), ("mfma_depth_bound", ctypes.c_int),
-                ("weights", ctypes.c_int), ("prologue", ctypes.c_int)]
+                ("weights", ctypes.c_int), ("prologue", ctypes.c_int),
+                ("int4_fp16", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -144,9 +146,10 @@ PROLOGUES = {None: 0, "rmsnorm": 1}
 
 
 def _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu=0, mfma=0,
-          weights="bf16", prologue=None):
+          weights="bf16", prologue=None, int4_fp16=0):
     return PlanOpts(int(splits), int(rows_per_wave), int(waves_per_block), int(unroll),
-                    int(waves_per_cu), int(mfma), WEIGHTS[weights], PROLOGUES[prologue])
+                    int(waves_per_cu), int(mfma), WEIGHTS[weights], PROLOGUES[prologue],
+                    int(int4_fp16))
 
 
 class Plan:
@@ -159,10 +162,11 @@ class Plan:
     def __init__(self, n: int, k: int, m: int = 1, device=None, *, splits: int = 0,
                  rows_per_wave: int = 0, waves_per_block: int = 0, unroll: int = 0,
                  waves_per_cu: int = 0, mfma: int = 0, weights: str = "bf16",
-                 prologue: str | None = None, desc: tuple | None = None):
+                 prologue: str | None = None, int4_fp16: int = 0,
+                 desc: tuple | None = None):
         self._h = ctypes.c_void_p()
         opts = _opts(splits, rows_per_wave, waves_per_block, unroll, waves_per_cu, mfma,
-                     weights, prologue)
+                     weights, prologue, int4_fp16)
         if desc is not None:
             d = DeviceDesc(int(desc[0]), float(desc[1]), float(desc[2]))
             st = _lib.gemv_plan_for(ctypes.byref(self._h), n, k, m, ctypes.byref(d),

@@ -1178,7 +1178,11 @@ extern "C" gemv_status gemv_plan(gemv_plan_t *out, int64_t n, int64_t k, int m, 
     if (st != GEMV_OK)
         return st;
     (*out)->device = device;
-    if ((*out)->waves_per_cu > 0) {
+    // The LDS reservation that enforces a resident-wave cap is for the bf16 kernels; INT4
+    // and RMSNorm plans size their LDS for what they stage, and a cap there only limits
+    // their grid.
+    if ((*out)->waves_per_cu > 0 && (*out)->weights == GEMV_WEIGHTS_BF16 &&
+        (*out)->prologue == 0) {
         st = fit_cap(*out, device);
         if (st != GEMV_OK) {
             gemv_plan_destroy(*out);

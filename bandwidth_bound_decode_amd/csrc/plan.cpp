@@ -160,30 +160,43 @@ int int4_depth_for(int64_t k)
 
 bool int4_tile_supported(int u, int r)
 {
-    return (r == 1 && (u == 1 || u == 2 || u == 4)) || (r == 2 && (u == 1 || u == 2));
+    return (r == 1 && (u == 1 || u == 2 || u == 4 || u == 7)) || (r == 2 && (u == 1 || u == 2));
 }
 
-// Tiles measured on MI355X (sweep at the six Llama shapes): x staged in LDS whenever it
-// fits, 8 waves per workgroup; rows of 4 or more wave steps one per wave in bursts of 4;
-// shorter rows in bursts of 2, two per wave (each x vector serves both) once N reaches
-// 16384 rows, one per wave below that. Without LDS, two rows per single-wave workgroup.
+// Tiles measured on MI355X (sweep of U, R, waves per workgroup, grid cap and the x staging
+// form at the six Llama shapes, graph replays of rotated weights). With x in LDS:
+//   - the burst is the whole row where the row's vectors per lane allow it (7 at K = 14336,
+//     2 at K = 4096), else 4, 2 or 1 vectors per lane;
+//   - rows of four or more vectors per lane, and short rows below 16384 outputs: one row
+//     per wave, 8 waves per workgroup, one workgroup per row block;
+//   - short rows from 16384 outputs on: two rows per wave sharing every x vector, 4 waves
+//     per workgroup, at most 32 waves per CU, the workgroups looping over row blocks;
+//   - the fp16 form of x only when a workgroup covers at least kInt4Fp16MinRows rows (the
+//     LM head), since its staging is paid once per workgroup.
+// Without LDS (x longer than 64 KiB staged), two rows per single-wave workgroup.
 gemv_status plan_int4(gemv_plan_t *out, int64_t n, int64_t k, int m,
                       const gemv_device_desc *dev, const gemv_plan_opts &o)
 {
-    if (m != 1 || k % kInt4VecElems != 0 || o.splits > 1 || o.mfma > 0 || o.waves_per_cu != 0)
+    if (m != 1 || k % kInt4VecElems != 0 || o.splits > 1 || o.mfma > 0 || o.waves_per_cu < 0 ||
+        o.waves_per_cu > kMaxWavesPerCU || o.int4_fp16 < -1 || o.int4_fp16 > 1)
         return GEMV_ERR_INVALID_ARG;
     const int64_t vecs = k / kInt4VecElems;
     const int64_t steps = ceil_div(vecs, kWaveLanes);
-    const bool xlds = 2 * k <= kInt4MaxLdsX;
-    int r, u, waves;
-    if (xlds && steps >= 4) {
-        r = 1;
-        u = 4;
-        waves = 8;
-    } else if (xlds) {
-        r = n >= kInt4TwoRowsFrom ? 2 : 1;
-        u = steps >= 2 ? 2 : 1;
-        waves = 8;
+    // x staged in LDS: 64 bytes of pairs and a 4-byte multiplier per 32-element vector
+    const int64_t x_lds = vecs * (64 + 4);
+    const bool xlds = x_lds <= kInt4MaxLdsX;
+    int r, u, waves, cap = 0;
+    if (xlds) {
+        u = steps == 7 ? 7 : steps >= 4 ? 4 : steps >= 2 ? 2 : 1;
+        if (steps < 4 && n >= kInt4TwoRowsFrom) {
+            r = 2;
+            u = u > 2 ? 2 : u;
+            waves = 4;
+            cap = kInt4ShortRowsCap;
+        } else {
+            r = 1;
+            waves = 8;
+        }
     } else {
         r = 2;
         u = 2;
@@ -195,7 +208,8 @@ gemv_status plan_int4(gemv_plan_t *out, int64_t n, int64_t k, int m,
         u = o.unroll;
     if (o.waves_per_block)
         waves = o.waves_per_block;
-    if (!int4_tile_supported(u, r) || !valid_waves(waves))
+    if (!int4_tile_supported(u, r) || !(valid_waves(waves) || waves == 16) ||
+        (!xlds && u == 7 && waves > 8))
         return GEMV_ERR_INVALID_ARG;
     const int depth = int4_depth_for(k);
     if (depth > kMaxDepth)
@@ -214,12 +228,28 @@ gemv_status plan_int4(gemv_plan_t *out, int64_t n, int64_t k, int m,
     p->waves_per_block = waves;
     p->unroll = u;
     p->slice = k;
-    p->grid_x = (int)ceil_div(n, (int64_t)r * waves);
+    // One workgroup per row block, or (waves_per_cu) at most that many resident waves' worth
+    // of workgroups per CU, each looping over row blocks so that its x staging serves them.
+    const int64_t row_blocks = ceil_div(n, (int64_t)r * waves);
+    int64_t grid = row_blocks;
+    const int waves_cap = o.waves_per_cu > 0 ? o.waves_per_cu : cap;
+    if (waves_cap > 0) {
+        const int64_t most = ceil_div((int64_t)dev->compute_units * waves_cap, waves);
+        if (most < grid)
+            grid = most;
+    }
+    p->grid_x = (int)grid;
     p->grid_y = 1;
     p->block_threads = kWaveLanes * waves;
     p->depth_bound = depth;
     p->weights = GEMV_WEIGHTS_INT4;
-    p->lds_bytes = xlds ? (int)(2 * k) : 0;   // the staged x
+    p->lds_bytes = xlds ? (int)x_lds : 0;   // the staged x
+    p->waves_per_cu = waves_cap;
+    // The fp16 form of the staged x costs its conversion once per workgroup and saves about
+    // a quarter of the unpacking per row: tried when a workgroup covers enough rows.
+    const int64_t rows_per_group = (int64_t)r * waves * ceil_div(row_blocks, grid);
+    p->int4_fp16 = xlds && (o.int4_fp16 > 0 ||
+                            (o.int4_fp16 == 0 && rows_per_group >= kInt4Fp16MinRows));
     int64_t per_cu = ceil_div((int64_t)p->grid_x * waves, dev->compute_units);
     if (per_cu > kMaxWavesPerCU)
         per_cu = kMaxWavesPerCU;
@@ -321,11 +351,12 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     // Row indices and grid sizes are held in 32 bits on the device.
     if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30)
         return GEMV_ERR_INVALID_ARG;
-    gemv_plan_opts o = {0, 0, 0, 0, 0, 0, 0, 0};
+    gemv_plan_opts o = {0, 0, 0, 0, 0, 0, 0, 0, 0};
     if (opts)
         o = *opts;
     if (o.splits < 0 || o.rows_per_wave < 0 || o.waves_per_block < 0 || o.unroll < 0 ||
-        o.waves_per_cu < -1 || o.waves_per_cu > kMaxWavesPerCU || o.mfma < -1 || o.mfma > 1)
+        o.waves_per_cu < -1 || o.waves_per_cu > kMaxWavesPerCU || o.mfma < -1 || o.mfma > 1 ||
+        (o.int4_fp16 != 0 && o.weights != GEMV_WEIGHTS_INT4))
         return GEMV_ERR_INVALID_ARG;
     if (o.prologue == GEMV_PROLOGUE_RMSNORM && o.weights == GEMV_WEIGHTS_BF16)
         return plan_rmsnorm(out, n, k, m, dev, o);
@@ -514,6 +545,7 @@ extern "C" gemv_status gemv_plan_query(gemv_plan_t p, gemv_plan_info *info)
     info->mfma_depth_bound = p->mfma_depth;
     info->weights = p->weights;
     info->prologue = p->prologue;
+    info->int4_fp16 = p->int4_fp16;
     return GEMV_OK;
 }
 

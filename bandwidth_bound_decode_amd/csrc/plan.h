@@ -47,6 +47,9 @@ constexpr int kInt4VecElems = 32;
 constexpr int kInt4Group = 128;
 constexpr int kInt4MaxLdsX = 64 * 1024;   // x staged in LDS up to this many bytes (2K)
 constexpr int64_t kInt4TwoRowsFrom = 16384;   // short INT4 rows: two per wave from this N
+constexpr int kInt4ShortRowsCap = 32;         // waves per CU for two-row short INT4 rows
+constexpr int64_t kInt4Fp16MinRows = 32;      // fp16 staging when a workgroup covers this
+                                              // many rows or more
 
 // One compiled (M, R, U) combination of the aligned fast-path kernel. The unaligned path
 // exists for every M and takes R at run time.
@@ -130,4 +133,5 @@ struct gemv_plan_s {
     int mfma_depth;
     int weights;                // GEMV_WEIGHTS_BF16 or GEMV_WEIGHTS_INT4
     int prologue;               // 0 or GEMV_PROLOGUE_RMSNORM
+    int int4_fp16;              // INT4 with x in LDS: the workgroups try the fp16 staging
 };

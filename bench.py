@@ -560,8 +560,21 @@ def main(argv=None):
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-shapes", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--sections", default="all",
+                    help="comma list of what to run besides the headline: shapes, rmsnorm, "
+                         "int4, decode, decode_int4, cpu (default: all)")
     args = ap.parse_args(argv)
     args.windows = max(5, args.windows)
+    every = {"shapes", "rmsnorm", "int4", "decode", "decode_int4", "cpu"}
+    wanted = every if args.sections == "all" else set(args.sections.split(","))
+    if wanted - every:
+        ap.error(f"unknown sections {sorted(wanted - every)}")
+    if args.skip_shapes:
+        wanted -= {"shapes", "rmsnorm", "int4"}
+    if args.skip_decode:
+        wanted -= {"decode", "decode_int4"}
+    if args.skip_cpu:
+        wanted -= {"cpu"}
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this GEMV build has no multi-GPU path "
@@ -647,7 +660,7 @@ def main(argv=None):
         "h100_context": H100,
     }
 
-    if not args.skip_cpu:
+    if "cpu" in wanted:
         t_cpu, threads = cpu_baseline(w, x)
         out["cpu_baseline"] = {"value": round(nb / t_cpu / 1e12, 6), "unit": "TB/s",
                                "cores": threads, "kind": "oracle",
@@ -658,7 +671,7 @@ def main(argv=None):
         log(f"cpu oracle: {t_cpu * 1e3:.1f} ms per GEMV on {threads} threads")
         out["cpu_baseline"]["per_config"] = oracle_per_config(workloads)
 
-    if not args.skip_shapes:
+    if "shapes" in wanted:
         shapes = []
         kproj = workloads.K_PROJ_AND_TAILS.gemvs[0]
         wkp, xkp = workloads.draw_config(workloads.K_PROJ_AND_TAILS)[0]
@@ -695,6 +708,7 @@ def main(argv=None):
             log(f"{name}: {r['us_per_launch']:.2f} us back to back, {r['TBps']:.3f} TB/s "
                 f"({r['pct_peak']:.1f} %)")
             out.setdefault("shapes", []).append(r)
+    if "rmsnorm" in wanted:
         # the RMSNorm prologue fused into the projections that consume the normalised x
         for name, segs in (("rmsnorm_qkv", (4096, 1024, 1024)), ("rmsnorm_gate_up", (14336, 14336))):
             r = bench_rmsnorm(torch, bbd, workloads, name, segs, 4096, args.shape_steps)
@@ -705,6 +719,7 @@ def main(argv=None):
                 f"{r['gemv_without_norm_us']:.2f} us, a separate norm launch "
                 f"{r['separate_torch_rms_norm_eager_us']:.2f} us")
             out.setdefault("rmsnorm_prologue", []).append(r)
+    if "int4" in wanted:
         # INT4 weights at the same projection shapes (batch 1)
         for name, n, k in (("int4_down", 4096, 14336), ("int4_k_proj", 1024, 4096),
                            ("int4_o_proj", 4096, 4096), ("int4_qkv", 6144, 4096),
@@ -717,7 +732,7 @@ def main(argv=None):
                 f"({r['pct_peak']:.1f} %)")
             out.setdefault("int4_shapes", []).append(r)
 
-    if not args.skip_decode:
+    if "decode" in wanted:
         d = bench_decode_step(torch, bbd, workloads, args.decode_replays, 3)
         for k in list(d):
             if isinstance(d[k], float):
@@ -729,6 +744,7 @@ def main(argv=None):
             f"{d['eager_ms_median']:.3f} ms; graph with {d['rmsnorm_prologue_calls']} fused "
             f"RMSNorm prologues {d['graph_with_rmsnorm_prologues_ms_median']:.3f} ms")
         torch.cuda.empty_cache()
+    if "decode_int4" in wanted:
         d4 = bench_decode_step_int4(torch, bbd, workloads, args.decode_replays)
         for k in list(d4):
             if isinstance(d4[k], float):

@@ -89,6 +89,8 @@ typedef struct {
     int mfma;
     int weights;        /* GEMV_WEIGHTS_BF16 (0) or GEMV_WEIGHTS_INT4; see gemv_int4_run */
     int prologue;       /* 0, or GEMV_PROLOGUE_RMSNORM; see gemv_rmsnorm_run */
+    int int4_fp16;      /* INT4 plans whose x is staged in LDS: 1 = try the fp16 form of the
+                           staged x, -1 = bf16 only, 0 = automatic (see gemv_int4_run) */
 } gemv_plan_opts;
 
 /* Input prologues a plan can be made for. */
@@ -135,6 +137,7 @@ typedef struct {
     int mfma_depth_bound;   /* h for that kernel, counting 32 roundings per MFMA */
     int weights;            /* the plan's weight format */
     int prologue;           /* the plan's input prologue (0: none) */
+    int int4_fp16;          /* INT4: 1 when the workgroups try the fp16 form of staged x */
 } gemv_plan_info;
 
 /*
@@ -256,9 +259,16 @@ gemv_status gemv_fused_run(gemv_plan_t p, const gemv_segment *segs, int nseg,
  *     accumulated in fp32 and overwritten, within the same tolerance as gemv_run.
  * The plan must come from gemv_plan / gemv_plan_for with opts.weights = GEMV_WEIGHTS_INT4,
  * m = 1 and k a multiple of 32 (whole 16-byte vectors; the last group may be short); it
- * never splits K, and opts.splits > 1, waves_per_cu and mfma = 1 are GEMV_ERR_INVALID_ARG.
- * rows_per_wave (1 or 2), unroll (1, 2 or 4; 1 or 2 with two rows) and waves_per_block may
- * be forced.
+ * never splits K, and opts.splits > 1 and mfma = 1 are GEMV_ERR_INVALID_ARG. rows_per_wave
+ * (1 or 2), unroll (1, 2, 4 or 7; 1 or 2 with two rows), waves_per_block (1, 2, 4, 8 or 16)
+ * and int4_fp16 may be forced; waves_per_cu > 0 caps the grid at that many waves per CU,
+ * each workgroup then looping over row blocks.
+ * When x fits in LDS (68 bytes per 32 elements, up to 64 KiB) the workgroup stages it once.
+ * With the fp16 form (int4_fp16) each 32-element vector of x is staged as fp16 x * 2^s, s
+ * its own power of two; a workgroup in which any element does not convert exactly (or x
+ * holds an inf or NaN) falls back to bf16. Both forms form every product exactly and meet
+ * the same tolerance, but round in a different order, so their results may differ in the
+ * last bits; for a fixed plan and x the result is reproducible.
  * Wq and X must be 16-byte aligned with ldq a multiple of 16 (>= k/2), S 2-byte and Y
  * 4-byte aligned (else GEMV_ERR_MISALIGNED); lds >= ceil(k/128); leading dimensions up
  * to 2^31 - 1. No workspace; no allocation or host synchronisation (capture-safe).

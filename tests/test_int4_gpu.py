@@ -49,7 +49,11 @@ def test_llama_shapes(n, k):
 
 TILES = [dict(), dict(unroll=1), dict(unroll=2, rows_per_wave=1, waves_per_block=1),
          dict(unroll=4, rows_per_wave=1, waves_per_block=8), dict(unroll=1, rows_per_wave=2),
-         dict(unroll=2, rows_per_wave=2, waves_per_block=2)]
+         dict(unroll=2, rows_per_wave=2, waves_per_block=2),
+         dict(unroll=2, rows_per_wave=1, waves_per_block=16),
+         # capped grids: workgroups loop over row blocks (their LDS holds only the staged x)
+         dict(unroll=2, rows_per_wave=1, waves_per_block=8, waves_per_cu=8),
+         dict(unroll=1, rows_per_wave=2, waves_per_block=16, waves_per_cu=16)]
 
 
 @pytest.mark.parametrize("n,k", [(7, 128), (33, 1024), (300, 4128), (64, 32), (5, 96),
@@ -63,18 +67,31 @@ def test_small_and_ragged(n, k):
         check(packed, scales, x, Y, f"int4 {n}x{k} {opts} lds={p.info['lds_bytes']}")
 
 
-def test_padded_strides_and_every_tile_same_bits():
+@pytest.mark.parametrize("form", [-1, 1])
+def test_padded_strides_and_every_tile_same_bits(form):
+    """Every compiled tile gives the same bits for one staging form of x (bf16: -1, fp16:
+    1), reproducibly; padding (0xEE bytes, NaN scales) is never read."""
     n, k = 100, 4128
-    packed, scales, _, x = draw(n, k, seed=5, ldq=2096, lds=40)   # padding: 0xEE bytes, NaN scales
+    packed, scales, _, x = draw(n, k, seed=5, ldq=2096, lds=40)
     ref = None
     for opts in TILES:
-        Y, _ = run(packed, scales, x, **opts)
-        check(packed, scales, x, Y, f"padded {opts}")
+        Y, p = run(packed, scales, x, int4_fp16=form, **opts)
+        assert p.info["int4_fp16"] == (form > 0)
+        check(packed, scales, x, Y, f"padded {opts} form {form}")
         if ref is None:
             ref = Y
         assert bits_equal(Y, ref), f"{opts} differs"
-        Y2, _ = run(packed, scales, x, **opts)
+        Y2, _ = run(packed, scales, x, int4_fp16=form, **opts)
         assert bits_equal(Y, Y2), "not reproducible"
+
+
+@pytest.mark.parametrize("n,k,form", [(4096, 14336, 1), (128256, 4096, -1), (28672, 4096, 1)])
+def test_llama_shapes_other_staging_form(n, k, form):
+    """The staging form the plan does not pick by default, at full size."""
+    packed, scales, _, x = draw(n, k, seed=n + k)
+    Y, p = run(packed, scales, x, int4_fp16=form)
+    assert p.info["int4_fp16"] == (form > 0)
+    check(packed, scales, x, Y, f"int4 {n}x{k} form {form}")
 
 
 def test_exact_cases():
@@ -91,16 +108,48 @@ def test_exact_cases():
     for c in (0, 1, 7, 8, 31, 32, 127, 128, 511, 1023):
         xo = torch.zeros((1, k), dtype=torch.bfloat16)
         xo[0, c] = 1.0
-        Y, _ = run(packed, scales, xo)
-        assert bits_equal(Y[0], torch.from_numpy(deq[:, c]).float()), f"one-hot column {c}"
+        for form in (-1, 1):
+            Y, _ = run(packed, scales, xo, int4_fp16=form)
+            assert bits_equal(Y[0], torch.from_numpy(deq[:, c]).float()), \
+                f"one-hot column {c}, form {form}"
     # every weight -8 with scale 2^-4 and x in {-2..2}: every partial sum is exact
     packed = torch.full((n, k // 2), 0x88, dtype=torch.uint8)
     scales = torch.full((n, k // 128), 2.0 ** -4, dtype=torch.bfloat16)
     xi = np.random.default_rng(9).integers(-2, 3, size=(1, k))
     x = torch.from_numpy(xi.astype(np.float32)).to(torch.bfloat16)
-    Y, _ = run(packed, scales, x)
     want = float(-8 * 2.0 ** -4 * xi.sum())
-    assert bits_equal(Y, torch.full((1, n), want)), Y[0, :3].tolist()
+    for form in (-1, 1):
+        Y, _ = run(packed, scales, x, int4_fp16=form)
+        assert bits_equal(Y, torch.full((1, n), want)), (form, Y[0, :3].tolist())
+
+
+@pytest.mark.parametrize("case", ["wide_range", "tiny_odd", "all_subnormal", "one_huge",
+                                  "boundary"])
+def test_x_staging_paths(case):
+    """x whose elements cannot all be staged as exact normal fp16 at one power-of-two scale
+    sends the workgroups to the bf16 form, and x that can takes the fp16 form; both must
+    meet the oracle, and the fp16 form must agree exactly where every sum is exact."""
+    n, k = 96, 4096
+    packed, scales, _, x = draw(n, k, seed=17)
+    xf = x.float()
+    if case == "wide_range":          # 2^40 next to O(1) values: the rest underflow in fp16
+        xf[0, 5] = 2.0 ** 40
+    elif case == "tiny_odd":          # an odd element 2^-26 below the largest (x 2^(s-4))
+        xf[0, 1] = xf.abs().max() * 2.0 ** -26
+    elif case == "all_subnormal":     # every element a bf16 subnormal
+        xf = torch.sign(xf) * 2.0 ** -130
+    elif case == "one_huge":          # a single huge element, zeros elsewhere: exact fp16
+        xf = torch.zeros_like(xf)
+        xf[0, 77] = 2.0 ** 100
+    elif case == "boundary":          # smallest odd element exactly at the normal fp16 edge
+        xf[0, 3] = xf.abs().max() * 2.0 ** -24
+    xb = xf.to(torch.bfloat16)
+    Y, _ = run(packed, scales, xb, int4_fp16=1)
+    check(packed, scales, xb, Y, f"x staging {case}")
+    if case == "one_huge":
+        deq = oracle.q4_dequant(packed.numpy(), host_bits(scales), k)
+        want = torch.from_numpy(deq[:, 77] * 2.0 ** 100).float()
+        assert bits_equal(Y[0], want)
 
 
 def test_graph_replay_matches_eager():

@@ -248,27 +248,43 @@ def test_mfma_plans():
 
 def test_int4_plans():
     """INT4 weights: batch 1, whole 32-weight vectors, no split and no workspace; x staged in
-    LDS when it fits; long rows one per wave in bursts of 4, short rows two per wave."""
+    LDS when it fits; a row's vectors in one burst where they allow it; short rows two per
+    wave from 16384 outputs, with a looping grid; the fp16 form of x only where a workgroup
+    covers 32 rows or more."""
     i = plan(4096, 14336, weights="int4").info
     assert i["weights"] == 1 and i["splits"] == 1 and i["mfma"] == 0
-    assert (i["rows_per_wave"], i["unroll"], i["waves_per_block"]) == (1, 4, 8)
-    assert (i["grid_x"], i["grid_y"], i["block_threads"], i["lds_bytes"]) == (512, 1, 512, 28672)
+    assert (i["rows_per_wave"], i["unroll"], i["waves_per_block"]) == (1, 7, 8)
+    assert i["int4_fp16"] == 0                     # 8 rows per workgroup
+    # the staged x: 64 bytes of fp16 pairs and a 4-byte multiplier per 32-element vector
+    assert (i["grid_x"], i["grid_y"], i["block_threads"], i["lds_bytes"]) == (512, 1, 512, 448 * 68)
     # 16 dot2 steps + 1, the scaled addition, 7 vectors per lane, 6 wave levels
     assert i["depth_bound"] == 17 + 1 + 7 + 6
     assert plan(4096, 14336, weights="int4").workspace_size == 0
     g = plan(28672, 4096, weights="int4").info
-    assert (g["rows_per_wave"], g["unroll"], g["waves_per_block"], g["grid_x"]) == (2, 2, 8, 1792)
+    # 32 waves per CU: 2048 four-wave workgroups over 3584 row blocks of 8 rows
+    assert (g["rows_per_wave"], g["unroll"], g["waves_per_block"], g["grid_x"]) == (2, 2, 4, 2048)
+    assert (g["waves_per_cu"], g["int4_fp16"]) == (32, 0)
+    lm = plan(128256, 4096, weights="int4").info   # 16032 row blocks: 64 rows per workgroup
+    assert (lm["rows_per_wave"], lm["unroll"], lm["waves_per_block"], lm["grid_x"]) == \
+        (2, 2, 4, 2048)
+    assert lm["int4_fp16"] == 1
     q = plan(6144, 4096, weights="int4").info
     assert (q["rows_per_wave"], q["unroll"], q["waves_per_block"], q["grid_x"]) == (1, 2, 8, 768)
+    assert plan(6144, 4096, weights="int4", int4_fp16=1).info["int4_fp16"] == 1
+    assert plan(128256, 4096, weights="int4", int4_fp16=-1).info["int4_fp16"] == 0
+    with pytest.raises(bbd.GemvError):
+        plan(6144, 4096, int4_fp16=1)               # a bf16 plan has no INT4 staging
     assert plan(7, 32, weights="int4").info["unroll"] == 1
-    big = plan(64, 65536, weights="int4").info                 # 128 KiB of x: no LDS
+    big = plan(64, 65536, weights="int4").info                 # 136 KiB of x: no LDS
     assert (big["lds_bytes"], big["rows_per_wave"], big["waves_per_block"]) == (0, 2, 1)
+    assert big["int4_fp16"] == 0
     f = plan(7, 4128, weights="int4", unroll=1, rows_per_wave=2, waves_per_block=2).info
     assert (f["unroll"], f["rows_per_wave"], f["waves_per_block"], f["grid_x"]) == (1, 2, 2, 2)
     assert plan(4096, 14336).info["weights"] == 0
     for bad in (dict(k=100), dict(m=2), dict(splits=2), dict(unroll=3), dict(unroll=8),
-                dict(rows_per_wave=4), dict(rows_per_wave=2, unroll=4), dict(waves_per_cu=8),
-                dict(waves_per_block=3), dict(mfma=1)):
+                dict(rows_per_wave=4), dict(rows_per_wave=2, unroll=4), dict(waves_per_cu=-1),
+                dict(waves_per_cu=33), dict(waves_per_block=3), dict(waves_per_block=32),
+                dict(mfma=1)):
         args = dict(n=64, k=4096, m=1)
         args.update({k: v for k, v in bad.items() if k in args})
         opts = {k: v for k, v in bad.items() if k not in args}
@@ -276,6 +292,11 @@ def test_int4_plans():
             plan(args["n"], args["k"], args["m"], weights="int4", **opts)
     with pytest.raises(bbd.GemvError):
         plan(64, 1 << 20, weights="int4")           # depth bound
+    # waves_per_cu caps the grid; the workgroups then loop over row blocks, and the LDS is
+    # still only the staged x
+    c = plan(4096, 14336, weights="int4", waves_per_cu=8).info
+    assert (c["grid_x"], c["lds_bytes"], c["waves_per_cu"]) == (256, 448 * 68, 8)
+    assert plan(4096, 14336, weights="int4", waves_per_block=16).info["grid_x"] == 256
 
 
 def test_rmsnorm_plans():
