@@ -4,9 +4,9 @@ The compute runs in hand-written gfx950 HIP kernels inside lib/libbbd_gemv.so (C
 include/gemv.h); this package is the thin ctypes binding over it.
 """
 from ._binding import (LIB_PATH, MAX_M, MAX_SEGMENTS, SIGNATURES, Chain, GemvError, Graph,
-                       Plan, Status, bytes_in_flight, fused_run, lib, rmsnorm_run, run,
-                       run_int4, run_static)
+                       Plan, Status, bytes_in_flight, fused_run, lib, read_stream, rmsnorm_run,
+                       run, run_int4, run_static)
 
 __all__ = ["LIB_PATH", "MAX_M", "MAX_SEGMENTS", "SIGNATURES", "Chain", "GemvError", "Graph",
-           "Plan", "Status", "bytes_in_flight", "fused_run", "lib", "rmsnorm_run", "run",
-           "run_int4", "run_static"]
+           "Plan", "Status", "bytes_in_flight", "fused_run", "lib", "read_stream",
+           "rmsnorm_run", "run", "run_int4", "run_static"]

@@ -107,6 +107,7 @@ SIGNATURES = {
     "gemv_chain_run": (_INT, [_P, _P]),
     "gemv_chain_check": (_INT, [_P]),
     "gemv_chain_destroy": (None, [_P]),
+    "gemv_read_stream": (_INT, [_P, _I64, _I64, _INT, _INT, _P, _P]),
     "gemv_status_string": (ctypes.c_char_p, [_INT]),
     "gemv_last_hip_error": (_INT, []),
 }
@@ -377,6 +378,17 @@ def fused_run(plan: Plan, segments, X: torch.Tensor, workspace: torch.Tensor | N
     st = _lib.gemv_fused_run(plan.handle, arr, len(segs), X.data_ptr(), _row_stride(X, "X"),
                              ws_ptr, ws_bytes, _stream_handle(stream))
     _check(st, "gemv_fused_run")
+
+
+def read_stream(buf: torch.Tensor, rows: int, row_bytes: int, unroll: int, waves_per_cu: int,
+                sink: torch.Tensor, stream=None):
+    """The pure-read streaming kernel (gemv_read_stream): `rows` rows of `row_bytes` bytes
+    from the device buffer `buf`, for measuring the read ceiling and bytes in flight."""
+    _on_gpu("gemv_read_stream", buf, sink)
+    if buf.numel() * buf.element_size() < rows * row_bytes or sink.numel() * sink.element_size() < 4:
+        raise ValueError("buffer smaller than rows * row_bytes, or sink under 4 bytes")
+    _check(_lib.gemv_read_stream(buf.data_ptr(), rows, row_bytes, unroll, waves_per_cu,
+                                 sink.data_ptr(), _stream_handle(stream)), "gemv_read_stream")
 
 
 class Graph:

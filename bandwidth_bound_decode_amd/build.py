@@ -30,7 +30,7 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror",
 
 
 RESOURCE_REPORT = os.path.join(LIB_DIR, "kernel_resources.json")
-HIP_UNITS = ("gemv", "whole", "batch", "mfma", "int4", "norm", "chain")
+HIP_UNITS = ("gemv", "whole", "batch", "mfma", "int4", "norm", "chain", "calib")
 REMARK = "[-Rpass-analysis=kernel-resource-usage]"
 
 

@@ -24,7 +24,10 @@ constexpr int kMinWavesPerCU = 1;       // no split while N / R gives this many 
 constexpr int kTargetWavesPerCU = 4;    // a split aims for this many waves per CU
 constexpr int64_t kMinSlice = 1024;     // never split K finer than this many elements
 constexpr int kMaxDepth = 160;          // gamma_160 (u = 2^-24) = 9.54e-6 < 1e-5
-constexpr double kDefaultLatency = 1.0e-6;   // assumed loaded HBM latency on MI355X
+// Loaded HBM latency on MI355X, measured with the pure-read stream (gemv_read_stream):
+// bytes in flight / rate is 0.40 us with 1 KiB in flight per CU and rises to ~0.66 us where
+// the rate reaches its ceiling (16-24 KiB per CU); the plans report Little's law with it.
+constexpr double kDefaultLatency = 0.65e-6;
 // Batch-1 resident-wave caps per CU (measured on MI355X, see the plan rule in plan.cpp):
 // rows longer than 8 wave steps stream best with at most 8 single-row waves per CU, in
 // equal rounds; short rows with more waves than one round holds, with at most 12.

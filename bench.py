@@ -148,13 +148,17 @@ def time_graph(torch, launch, count: int, stream):
 def time_windows(torch, launch, per_graph: int, windows: int, min_launches: int, stream):
     """Per-launch time of `launch` run back to back, independent of the graph size.
 
-    The `per_graph` launches are captured into one graph on `stream`. Each of `windows`
-    windows replays it `reps` times back to back (enough replays for >= `min_launches`
-    launches), bracketed by HIP events on `stream`; the per-launch time of a window is its
-    span over reps * per_graph. Each window is followed by one single-replay window, whose
+    The launches are captured into one graph on `stream`: `per_graph` of them, repeated to a
+    whole multiple of `per_graph` that reaches `min_launches`. Each of `windows` windows
+    replays it back to back (once, or as often as needed for `min_launches` launches),
+    bracketed by HIP events on `stream`; the per-launch time of a window is its span over
+    the launches in it. Each window is followed by one single-replay window, whose
     excess over per_graph launches is the replay's own overhead (graph submission and the
     events), reported apart. Returns a dict of medians and the per-window figures."""
     import bandwidth_bound_decode_amd as bbd
+    # One graph holds a whole multiple of the K launches, at least min_launches of them, so
+    # that the replay's own cost is spread over as many launches whatever K is.
+    per_graph = per_graph * max(1, math.ceil(min_launches / per_graph))
     g = bbd.Graph(stream)
     with torch.cuda.stream(stream):
         with g:
@@ -483,6 +487,64 @@ def cpu_baseline(w, x, runs=3):
     return t, threads
 
 
+def read_calibration(torch, bbd, cus, steps, window_launches):
+    """The achievable read ceiling and the loaded latency, from the library's pure-read
+    streaming kernel (the GEMV's weight stream alone).
+
+    Sweep: 2 GiB read in 64 KiB rows (far beyond the 256 MB Infinity Cache), for U loads in
+    flight per lane and a cap of W resident single-wave workgroups per CU; bytes in flight
+    on the chip = W * U * 1 KiB * CUs. The ceiling is the best rate; on the points well
+    below it (linear part) Little's law gives latency = bytes in flight / rate. Also the
+    same read at the headline's shape (4096 rows of 28 KiB, U = 4, W = 8, rotated over
+    >= 1 GB of copies), timed like the headline: the floor the GEMV's schedule allows."""
+    rows, row_bytes = 32768, 65536
+    buf = torch.empty(rows * row_bytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    sweep = []
+    for u in (1, 2, 4, 8):
+        for cap in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32):
+            tw = time_windows(torch, lambda i: bbd.read_stream(buf, rows, row_bytes, u, cap,
+                                                               sink, side), 5, 5, 5, side)
+            rate = rows * row_bytes / tw["launch_s"]
+            inflight = cap * u * 1024 * cus
+            sweep.append({"unroll": u, "waves_per_cu": cap, "inflight_kib_per_cu": cap * u,
+                          "TBps": round(rate / 1e12, 4),
+                          "latency_us": round(inflight / rate * 1e6, 4)})
+    del buf
+    torch.cuda.empty_cache()
+    ceiling = max(p["TBps"] for p in sweep)
+    best = max(sweep, key=lambda p: p["TBps"])
+    linear = [p for p in sweep if p["TBps"] < 0.75 * ceiling]
+    lat_fit = statistics.median(p["latency_us"] for p in linear)
+    # the least bytes in flight per CU that reach 95 % of the ceiling, and the latency there
+    knee = min((p for p in sweep if p["TBps"] >= 0.95 * ceiling),
+               key=lambda p: p["inflight_kib_per_cu"])
+    # the headline's rows read alone
+    nrows, rb = 4096, 14336 * 2
+    copies = max(2, math.ceil(ROTATION_BYTES / (nrows * rb)) + 1)
+    arena = torch.empty(copies * nrows * rb, dtype=torch.uint8, device="cuda")
+    arena.fill_(0x3C)
+    views = [arena[i * nrows * rb:(i + 1) * nrows * rb] for i in range(copies)]
+    tw = time_windows(torch, lambda i: bbd.read_stream(views[i % copies], nrows, rb, 4, 8, sink,
+                                                       side), steps, 5, window_launches, side)
+    del arena, views
+    torch.cuda.empty_cache()
+    return {"TBps": ceiling, "frac_of_peak": round(ceiling * 1e12 / PEAK_HBM, 4),
+            "best": {"unroll": best["unroll"], "waves_per_cu": best["waves_per_cu"]},
+            "latency_us_linear_median": round(lat_fit, 4),
+            "latency_us_light": min(p["latency_us"] for p in sweep),
+            "knee": knee,
+            "headline_shape_read_us": round(tw["launch_s"] * 1e6, 3),
+            "headline_shape_read_TBps": round(nrows * rb / tw["launch_s"] / 1e12, 4),
+            "sweep": sweep,
+            "method": "2 GiB in 64 KiB rows, gemv_read_stream (one single-wave workgroup per "
+                      "row, U nontemporal 16-byte loads per lane per burst, at most W "
+                      "workgroups per CU); latency = bytes in flight / rate below 75 % of "
+                      "the ceiling"}
+
+
 def oracle_per_config(workloads, runs=3):
     """The oracle on every workload, on 1 thread and on all host threads: 1 untimed run then
     the median of `runs`. The decode step is sampled as one layer (QKV, o_proj, gate_up, down)
@@ -561,11 +623,11 @@ def main(argv=None):
     ap.add_argument("--skip-shapes", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--sections", default="all",
-                    help="comma list of what to run besides the headline: shapes, rmsnorm, "
-                         "int4, decode, decode_int4, cpu (default: all)")
+                    help="comma list of what to run besides the headline: calib, shapes, "
+                         "rmsnorm, int4, decode, decode_int4, cpu (default: all)")
     args = ap.parse_args(argv)
     args.windows = max(5, args.windows)
-    every = {"shapes", "rmsnorm", "int4", "decode", "decode_int4", "cpu"}
+    every = {"calib", "shapes", "rmsnorm", "int4", "decode", "decode_int4", "cpu"}
     wanted = every if args.sections == "all" else set(args.sections.split(","))
     if wanted - every:
         ap.error(f"unknown sections {sorted(wanted - every)}")
@@ -629,18 +691,21 @@ def main(argv=None):
                    "n": g.n, "k": g.k, "m": g.m, "sigma_w": workloads.SIGMA_W,
                    "sigma_x": workloads.SIGMA_X, "seed": cfg.seed,
                    "rotation_copies": res["rotation_copies"], "plan": plan.info},
-        "timing": {"method": "the K steps (one rotated launch each) captured in one graph; "
-                             "each window replays it back to back enough times for "
-                             f">= {args.window_launches} launches between two HIP events on "
-                             "the replay stream; value and ms_per_step use the median window",
+        "timing": {"method": "the K steps (one rotated launch each), repeated to a whole "
+                             f"multiple of K of at least {args.window_launches} launches, "
+                             "captured in one graph; each window is one replay between two HIP "
+                             "events on the replay stream; value and ms_per_step use the "
+                             "median window",
+                   "launches_per_graph": tw["per_graph"],
                    "windows": tw["windows"], "launches_per_window": tw["reps"] * tw["per_graph"],
                    "timed_launches": tw["timed_launches"],
                    "per_window_us": [round(t * 1e6, 4) for t in tw["per_window_s"]],
                    "window_spread": round(tw["spread"], 5),
                    "replay_overhead_us": round(tw["replay_overhead_s"] * 1e6, 3),
-                   "replay_overhead_note": "one replay of the K-launch graph from an idle "
-                                           "stream minus K back-to-back launches: graph "
-                                           "submission and event cost, paid once per replay"},
+                   "replay_overhead_note": "one replay of the graph from an idle stream "
+                                           "minus its launches at the back-to-back rate: "
+                                           "graph submission and event cost, paid once per "
+                                           "replay"},
         "pct_of_peak": round(100 * value_TBps * 1e12 / PEAK_HBM, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved_GBps, 1), "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": round(achieved_GBps * 1e9 / PEAK_HBM, 4),
@@ -659,6 +724,18 @@ def main(argv=None):
                    "peak_hbm_TBps_assumed": PEAK_HBM / 1e12},
         "h100_context": H100,
     }
+
+    if "calib" in wanted:
+        cal = read_calibration(torch, bbd, props.multi_processor_count, args.steps,
+                               args.window_launches)
+        out["read_ceiling"] = cal
+        out["pct_of_read_ceiling"] = round(100 * value_TBps / cal["TBps"], 2)
+        out["roofline"]["frac_of_read_ceiling"] = round(value_TBps / cal["TBps"], 4)
+        log(f"read ceiling {cal['TBps']:.3f} TB/s at U={cal['best']['unroll']} "
+            f"W={cal['best']['waves_per_cu']}; loaded latency {cal['latency_us_linear_median']:.3f} us "
+            f"(linear part), knee {cal['knee']['inflight_kib_per_cu']} KiB/CU; headline rows read "
+            f"alone {cal['headline_shape_read_us']:.2f} us; GEMV at "
+            f"{out['pct_of_read_ceiling']:.1f} % of the ceiling")
 
     if "cpu" in wanted:
         t_cpu, threads = cpu_baseline(w, x)

@@ -371,6 +371,23 @@ gemv_status gemv_chain_check(gemv_chain_t c);
 /* Release a chain and its device memory (NULL is allowed). */
 void gemv_chain_destroy(gemv_chain_t c);
 
+/*
+ * Measurement support, not part of the GEMV: read `rows` rows of `row_bytes` bytes from the
+ * device buffer `buf` (row r at buf + r * row_bytes) with the batch-1 GEMV's weight stream
+ * and nothing else - one single-wave workgroup per row, each lane issuing `unroll` (1, 2, 4
+ * or 8) nontemporal 16-byte loads before using any, lanes 16 bytes apart - with at most
+ * `waves_per_cu` (1..31; 0 or 32: no cap) such workgroups resident on a CU. Over a buffer
+ * much larger than the caches its rate is the achievable read ceiling; a sweep of unroll
+ * and waves_per_cu gives bandwidth against bytes in flight, whose linear part has the
+ * loaded latency as its slope (Little's law: decode-GEMV page, "A strong answer"; GPU
+ * performance chains page, "Bytes in flight to reach bandwidth"). row_bytes must be a
+ * multiple of 1024 * unroll, buf 16-byte and sink 4-byte aligned; the words read are
+ * folded together and the fold is stored to *sink only if it equals one fixed value, which
+ * keeps the loads from being dropped. Asynchronous on `stream`; allocates nothing.
+ */
+gemv_status gemv_read_stream(const void *buf, int64_t rows, int64_t row_bytes, int unroll,
+                             int waves_per_cu, unsigned *sink, void *stream);
+
 /* A static description of a status code ("unknown status" for anything else). */
 const char *gemv_status_string(gemv_status s);
 

@@ -324,3 +324,23 @@ def test_static_entry_point_refuses_before_any_hip_call():
         lib.gemv_plan_destroy(h)
     assert lib.gemv_run_static(None, FAKE, 4096, FAKE, 4096, FAKE, 64, None) == \
         Status.INVALID_ARG
+
+
+def test_read_stream_validation_before_any_hip_call():
+    lib = bbd.lib()
+    sink = FAKE + 64
+    ok = dict(buf=FAKE, rows=8, row_bytes=4096, unroll=4, waves=8, sink=sink)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.gemv_read_stream(a["buf"], a["rows"], a["row_bytes"], a["unroll"],
+                                    a["waves"], a["sink"], None)
+    assert call(buf=None) == Status.INVALID_ARG
+    assert call(sink=None) == Status.INVALID_ARG
+    assert call(rows=0) == Status.INVALID_ARG
+    assert call(row_bytes=4096 + 1024) == Status.INVALID_ARG     # not a multiple of 1 KiB * U
+    assert call(unroll=3) == Status.INVALID_ARG
+    assert call(waves=33) == Status.INVALID_ARG
+    assert call(waves=-1) == Status.INVALID_ARG
+    assert call(buf=FAKE + 8) == Status.MISALIGNED
+    assert call(sink=sink + 2) == Status.MISALIGNED
