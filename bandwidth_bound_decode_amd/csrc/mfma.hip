@@ -14,17 +14,29 @@
 // goes to lane group g of MFMA u: each 16-byte load then covers 64 contiguous bytes of 16
 // rows (of W) or of 16 vectors (of X).
 //
-// Work split (measured on MI355X at 4096 x 14336, M = 8..16; probe sweep of tiles per wave,
-// MFMAs per burst, waves per workgroup and split counts):
-//   - a workgroup owns 32 rows (two 16-row tiles, which share every X fragment, halving X
-//     traffic against one tile) and one K slice; its 8 waves take the slice's 64-element
-//     chunks in turn, starting at a per-workgroup rotation so that workgroups running side
-//     by side read different column ranges of their rows;
-//   - per chunk a wave loads both tiles' W and the chunk's X (six 16-byte loads per lane)
-//     before its four MFMAs; W goes through the cache like X (for this access pattern the
-//     streaming hint measured slower);
+// Work split (measured on MI355X at 4096 x 14336, M = 8..16; probe sweeps of tiles per
+// workgroup, chunk sizes, MFMAs per burst, waves per workgroup and split counts):
+//   - a workgroup owns T 16-row tiles and one K slice; its 8 waves take the slice's chunks
+//     in turn, starting at a per-workgroup rotation so that workgroups running side by
+//     side read different column ranges of their rows. Two forms: T = 2 with 64-element
+//     chunks for any M up to 16 (the two tiles share every X fragment, halving X traffic
+//     against one tile), and, for M <= 8, T = 1 with 128-element chunks, whose X is only
+//     8 vectors: twice the row blocks, so 4096 rows fill 256 CUs with no split and no
+//     combine (19.8 us against 21.1 us at M = 8);
+//   - a chunk row is one or two 128-byte lines. Loaded straight in the operand layout,
+//     every load instruction touches 16 rows x 64 bytes (half of 16 cache lines); a
+//     read-only probe of that pattern streamed W at 4.3-5.7 TB/s against 6.4 TB/s for
+//     whole lines. So the wave moves the chunk into a private LDS buffer with direct
+//     global-to-LDS loads that each cover one line of 8 rows (W with the streaming hint),
+//     then reads the operands from LDS. Load lane l takes row l / 8 of its 8 and the
+//     16-byte piece (l % 8) ^ (l / 8) of that row's line, and writes LDS slot l; the XOR
+//     puts the 8 rows an operand read gathers in 8 different bank groups. MFMA u of a
+//     chunk takes K elements 32 u + 8 g .. + 8 in lane group g, i.e. piece 4 (u % 2) + g of
+//     line u / 2, on both the A and the B side;
+//   - per chunk: the direct loads, the wait for them, the LDS operand reads, the next
+//     chunk's loads (once the reads are in registers), then the MFMAs;
 //   - the 8 waves' partial tiles are summed in LDS in wave order, then stored; a plan that
-//     splits K (too few 32-row blocks for the CUs) stores device-coherent partials and the
+//     splits K (too few row blocks for the CUs) stores device-coherent partials and the
 //     last workgroup of a row block to arrive adds them in slice order, as the VALU
 //     kernels' split combine does.
 // The order of every sum is fixed, so results are reproducible bit for bit; they differ in
@@ -42,10 +54,15 @@ using namespace bbd;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kTiles = kMfmaRowsPerBlock / 16;   // 16-row tiles per workgroup
-constexpr int kU = kMfmaChunk / 32;              // MFMAs per chunk and tile
 constexpr int kThreads = kWaveLanes * kMfmaWaves;
+constexpr int kLineRows = 8;                     // rows (or X vectors) per direct load
+constexpr int kLineElems = 64;                   // bf16 elements in a 128-byte line
+constexpr int kCachePolicyNT = 2;                // the streaming hint on a direct load
+constexpr int kWaitVmOnly = 0x0F70;              // s_waitcnt vmcnt(0)
+constexpr int kWaitLgkmOnly = 0xC07F;            // s_waitcnt lgkmcnt(0)
 
 __device__ __forceinline__ floatx4 mfma(u32x4 a, u32x4 b, floatx4 c)
 {
@@ -53,64 +70,115 @@ __device__ __forceinline__ floatx4 mfma(u32x4 a, u32x4 b, floatx4 c)
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// y[m][row] = sum_k w[row][k] x[m][k] for the 32-row block blockIdx.x and the K slice
-// blockIdx.y (of gridDim.y). With one slice the result goes to y; with several, to
-// partial[slice][m][row] and then, by the last arrival, to y.
+// y[m][row] = sum_k w[row][k] x[m][k] for the row block blockIdx.x (T 16-row tiles) and
+// the K slice blockIdx.y (of gridDim.y), in chunks of CH elements. XV: X vectors staged
+// per chunk (16, or 8 when M <= 8: B lanes 8..15 then repeat vectors 0..7, and their
+// output columns are never stored). With one slice the result goes to y; with several,
+// to partial[slice][m][row] and then, by the last arrival, to y.
+template <int T, int XV, int CH>
 __global__ void __launch_bounds__(kThreads)
     gemv_mfma(const uint16_t *w, const uint16_t *x, float *y, float *partial,
               unsigned *tickets, int n, int k, int ldw, int ldx, int ldy, int m, int slice)
 {
-    __shared__ floatx4 red[kMfmaWaves - 1][kTiles][kWaveLanes];
+    constexpr int kRows = 16 * T;                    // rows per workgroup
+    constexpr int kLines = CH / kLineElems;          // 128-byte lines per row per chunk
+    constexpr int kU = CH / 32;                      // MFMAs per tile per chunk
+    constexpr int kWGroups = kRows / kLineRows;      // 8-row groups of W
+    constexpr int kXGroups = XV / kLineRows;         // 8-vector groups of X
+    constexpr int kWLoads = kWGroups * kLines;
+    constexpr int kXLoads = kXGroups * kLines;
+    static_assert(CH % kLineElems == 0 && (XV == 8 || XV == 16), "unsupported form");
+    __shared__ floatx4 red[kMfmaWaves - 1][T][kWaveLanes];
+    // Each wave's chunk: load j = group * kLines + line (1 KiB each), W groups first.
+    __shared__ u32x4 stage[kMfmaWaves][kWLoads + kXLoads][kWaveLanes];
     __shared__ unsigned s_last;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int i16 = lane & 15, g = lane >> 4;
     const int splits = gridDim.y, s = blockIdx.y;
-    const int row0 = blockIdx.x * kMfmaRowsPerBlock;
+    const int row0 = blockIdx.x * kRows;
     const int k0 = s * slice;
-    const int chunks = min(slice, k - k0) / kMfmaChunk;
+    const int chunks = min(slice, k - k0) / CH;
 
-    const uint16_t *wr[kTiles];
+    // Load side: row (or vector) lr of each group, piece lq of each of its lines.
+    const int lr = lane >> 3, lq = (lane & 7) ^ lr;
+    const uint16_t *gw[kWGroups];
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t)
-        wr[t] = w + (int64_t)min(row0 + 16 * t + i16, n - 1) * ldw + k0 + 8 * g;
-    const uint16_t *xr = x + (int64_t)min(i16, m - 1) * ldx + k0 + 8 * g;
+    for (int j = 0; j < kWGroups; ++j)   // rows past N re-read row N-1; never stored
+        gw[j] = w + (int64_t)min(row0 + kLineRows * j + lr, n - 1) * ldw + k0 + 8 * lq;
+    const uint16_t *gx[kXGroups];
+#pragma unroll
+    for (int j = 0; j < kXGroups; ++j)   // vectors past M repeat the last one
+        gx[j] = x + (int64_t)min(kLineRows * j + lr, m - 1) * ldx + k0 + 8 * lq;
+    // Read side: operand lane (i16, g) of MFMA u takes piece 4 (u % 2) + g of line u / 2 of
+    // row i16, which group i16 / 8 (of its tile, or of X) left in slot
+    // 8 (i16 % 8) + ((4 (u % 2) + g) ^ (i16 % 8)).
+    const int ri = i16 & 7, hj = i16 >> 3;
+    const int xg = kXGroups == 2 ? hj : 0;
+    int slot[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        slot[h] = kLineRows * ri + ((4 * h + g) ^ ri);
+    u32x4 (&buf)[kWLoads + kXLoads][kWaveLanes] = stage[wave];
 
     const int turns = (chunks - wave + kMfmaWaves - 1) / kMfmaWaves;
     const int rot = (int)((blockIdx.x * 37u + (unsigned)s * 11u) % (unsigned)chunks);
-    floatx4 acc[kTiles];
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t)
-        acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < turns; ++i) {
+    auto issue = [&](int i) {
         int c = wave + i * kMfmaWaves + rot;
         c = c >= chunks ? c - chunks : c;
-        u32x4 a[kTiles][kU], b[kU];
+#pragma unroll
+        for (int j = 0; j < kWGroups; ++j)
+#pragma unroll
+            for (int l = 0; l < kLines; ++l)
+                __builtin_amdgcn_global_load_lds(
+                    (global_void *)(gw[j] + c * CH + kLineElems * l),
+                    (lds_void *)&buf[j * kLines + l][0], 16, 0, kCachePolicyNT);
+#pragma unroll
+        for (int j = 0; j < kXGroups; ++j)
+#pragma unroll
+            for (int l = 0; l < kLines; ++l)
+                __builtin_amdgcn_global_load_lds(
+                    (global_void *)(gx[j] + c * CH + kLineElems * l),
+                    (lds_void *)&buf[kWLoads + j * kLines + l][0], 16, 0, 0);
+    };
+    floatx4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (turns > 0)
+        issue(0);
+    for (int i = 0; i < turns; ++i) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmOnly);   // this chunk's lines have landed
+        u32x4 a[T][kU], b[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                a[t][u] = buf[(2 * t + hj) * kLines + u / 2][slot[u & 1]];
+            b[u] = buf[kWLoads + xg * kLines + u / 2][slot[u & 1]];
+        }
+        // The buffer is free once the reads are in registers; then the next chunk goes out.
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmOnly);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < turns)
+            issue(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kU; ++u)
 #pragma unroll
-            for (int t = 0; t < kTiles; ++t)
-                a[t][u] = load_cached(wr[t] + c * kMfmaChunk + 32 * u);
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-            b[u] = load_cached(xr + c * kMfmaChunk + 32 * u);
-        __builtin_amdgcn_sched_barrier(0);   // every load of the chunk before the first MFMA
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-#pragma unroll
-            for (int t = 0; t < kTiles; ++t)
+            for (int t = 0; t < T; ++t)
                 acc[t] = mfma(a[t][u], b[u], acc[t]);
     }
 
     if (wave > 0) {
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t)
+        for (int t = 0; t < T; ++t)
             red[wave - 1][t][lane] = acc[t];
     }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
+        for (int t = 0; t < T; ++t) {
 #pragma unroll
             for (int v = 0; v < kMfmaWaves - 1; ++v)
                 acc[t] += red[v][t][lane];
@@ -145,7 +213,7 @@ __global__ void __launch_bounds__(kThreads)
     __syncthreads();
     if (!s_last)
         return;
-    const int rows = min(kMfmaRowsPerBlock, n - row0);
+    const int rows = min(kRows, n - row0);
     const int64_t plane = (int64_t)m * n;
     for (int t = threadIdx.x; t < rows * m; t += kThreads) {
         const int mi = t / rows;
@@ -185,7 +253,13 @@ gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const
     int n = (int)p->n, k = (int)p->k, ldw = (int)segs[0].ldw, ldxi = (int)ldx,
         ldy = (int)segs[0].ldy, m = p->m, slice = (int)p->mfma_slice;
     void *args[] = {&w, &x, &y, &partial, &tickets, &n, &k, &ldw, &ldxi, &ldy, &m, &slice};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(gemv_mfma),
+    const bool narrow = p->mfma_rows == kMfmaNarrowRows;
+    if ((!narrow && p->mfma_rows != kMfmaRowsPerBlock) || (narrow && m > kMfmaNarrowMaxBatch))
+        return GEMV_ERR_INVALID_ARG;
+    const void *fn = narrow
+                         ? reinterpret_cast<const void *>(&gemv_mfma<1, 8, kMfmaNarrowChunk>)
+                         : reinterpret_cast<const void *>(&gemv_mfma<2, 16, kMfmaChunk>);
+    hipError_t e = hipLaunchKernel(fn,
                                    dim3((unsigned)p->mfma_grid_x, (unsigned)p->mfma_splits),
                                    dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GEMV_OK : record_hip_error((int)e, GEMV_ERR_DEVICE);

@@ -138,13 +138,13 @@ int depth_for(int64_t slice, int s)
 // The same bound for the matrix-core kernel. The instruction's internal summation order is
 // not documented, so a product is charged 32 roundings inside the MFMA it enters (as if the
 // 32 products of a 16x16x32 step were added one at a time) and the running accumulator one
-// rounding per later MFMA of the wave's chain (two per 64-element chunk); then the 7 adds
-// of the other waves' partial tiles and S-1 combine additions.
-int mfma_depth_for(int64_t slice, int s)
+// rounding per later MFMA of the wave's chain (chunk / 32 per chunk); then the 7 adds of
+// the other waves' partial tiles and S-1 combine additions.
+int mfma_depth_for(int64_t slice, int s, int chunk)
 {
-    int64_t chunks = ceil_div(slice, kMfmaChunk);
+    int64_t chunks = ceil_div(slice, chunk);
     int64_t turns = ceil_div(chunks, kMfmaWaves);
-    return (int)(32 + (kMfmaChunk / 32) * turns + (kMfmaWaves - 1) + (s - 1));
+    return (int)(32 + (chunk / 32) * turns + (kMfmaWaves - 1) + (s - 1));
 }
 
 bool valid_waves(int w) { return w == 1 || w == 2 || w == 4 || w == 8; }
@@ -443,26 +443,31 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
         }
     }
 
-    // Matrix-core launch for batches: 32-row workgroups, split over K (with the same
-    // deterministic combine) only while the row blocks alone leave CUs without one.
+    // Matrix-core launch for batches: 16-row workgroups with 128-element chunks for M <= 8
+    // (K a multiple of 128), else 32-row workgroups with 64-element chunks; split over K
+    // (with the same deterministic combine) only while the row blocks alone leave CUs
+    // without one.
     int mf = 0, mf_s = 1, mf_depth = 0;
     int64_t mf_slice = k;
-    const int64_t mf_grid = ceil_div(n, kMfmaRowsPerBlock);
+    const bool narrow = m <= kMfmaNarrowMaxBatch && k % kMfmaNarrowChunk == 0;
+    const int mf_rows = narrow ? kMfmaNarrowRows : kMfmaRowsPerBlock;
+    const int mf_chunk = narrow ? kMfmaNarrowChunk : kMfmaChunk;
+    const int64_t mf_grid = ceil_div(n, mf_rows);
     {
         const bool forced = o.splits || o.rows_per_wave || o.waves_per_block || o.unroll ||
                             o.waves_per_cu;
         const bool want_mf = o.mfma > 0 ? m >= 2 : o.mfma == 0 && m >= kMfmaMinBatch && !forced;
-        if (want_mf && k % kMfmaChunk == 0) {
+        if (want_mf && k % mf_chunk == 0) {
             int64_t want = mf_grid >= dev->compute_units ? 1 : ceil_div(dev->compute_units, mf_grid);
-            int64_t cap = k / kMfmaChunk / kMfmaWaves;   // every wave keeps a chunk per slice
+            int64_t cap = k / mf_chunk / kMfmaWaves;   // every wave keeps a chunk per slice
             if (want > cap)
                 want = cap > 1 ? cap : 1;
             if (want > kMaxSplits)
                 want = kMaxSplits;
             for (int cand = (int)want; cand <= kMaxSplits; ++cand) {
-                mf_slice = round_up(ceil_div(k, cand), kMfmaChunk);
+                mf_slice = round_up(ceil_div(k, cand), mf_chunk);
                 mf_s = (int)ceil_div(k, mf_slice);
-                mf_depth = mfma_depth_for(mf_slice, mf_s);
+                mf_depth = mfma_depth_for(mf_slice, mf_s, mf_chunk);
                 if (mf_depth <= kMaxDepth)
                     break;
             }
@@ -493,6 +498,7 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     p->mfma_slice = mf ? mf_slice : 0;
     p->mfma_grid_x = mf ? (int)mf_grid : 0;
     p->mfma_depth = mf ? mf_depth : 0;
+    p->mfma_rows = mf ? mf_rows : 0;
     const int ws_splits = mf && mf_s > s ? mf_s : s;
     if (ws_splits > 1) {
         // One arrival ticket per row block (in a fixed-size region), then S x M x N fp32
@@ -543,6 +549,7 @@ extern "C" gemv_status gemv_plan_query(gemv_plan_t p, gemv_plan_info *info)
     info->mfma_slice = p->mfma_slice;
     info->mfma_grid_x = p->mfma_grid_x;
     info->mfma_depth_bound = p->mfma_depth;
+    info->mfma_rows = p->mfma_rows;
     info->weights = p->weights;
     info->prologue = p->prologue;
     info->int4_fp16 = p->int4_fp16;

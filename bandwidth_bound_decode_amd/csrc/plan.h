@@ -39,12 +39,19 @@ constexpr int kOneRoundWavesPerCU = 16;   // short rows: up to this many waves p
 // many slots, so that plans with up to this many row blocks can share one workspace in any
 // order without one plan's partial sums landing on another plan's tickets.
 constexpr int64_t kTicketSlots = 4096;
-// Matrix-core kernel (mfma.hip): 32-row workgroups of 8 waves that take K in chunks of 64
-// elements; used by default from this batch size on (measured crossover at 4096 x 14336).
+// Matrix-core kernel (mfma.hip): workgroups of 8 waves that take K in chunks; used by
+// default from this batch size on (at 4096 x 14336 it is faster than the VALU kernels from
+// M = 2 on: 19.3 against 19.9 us, and 19.8 against 24.4 us at M = 8). Two forms: 32-row
+// blocks with 64-element chunks (any M up to 16), and for M <= 8 16-row blocks with
+// 128-element chunks, whose X is half as many vectors per chunk (measured faster there:
+// twice the row blocks, so 4096 rows fill 256 CUs without a split).
 constexpr int kMfmaRowsPerBlock = 32;
-constexpr int kMfmaWaves = 8;
 constexpr int kMfmaChunk = 64;
-constexpr int kMfmaMinBatch = 8;
+constexpr int kMfmaNarrowRows = 16;
+constexpr int kMfmaNarrowChunk = 128;
+constexpr int kMfmaNarrowMaxBatch = 8;
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaMinBatch = 2;
 // INT4 weights (int4.hip): 32 weights per 16-byte vector, one bf16 scale per 128.
 constexpr int kInt4VecElems = 32;
 constexpr int kInt4Group = 128;
@@ -134,6 +141,7 @@ struct gemv_plan_s {
     int64_t mfma_slice;
     int mfma_grid_x;
     int mfma_depth;
+    int mfma_rows;              // rows per matrix-core workgroup: 32, or 16 (M <= 8)
     int weights;                // GEMV_WEIGHTS_BF16 or GEMV_WEIGHTS_INT4
     int prologue;               // 0 or GEMV_PROLOGUE_RMSNORM
     int int4_fp16;              // INT4 with x in LDS: the workgroups try the fp16 staging

@@ -150,11 +150,14 @@ def time_windows(torch, launch, per_graph: int, windows: int, min_launches: int,
 
     The launches are captured into one graph on `stream`: `per_graph` of them, repeated to a
     whole multiple of `per_graph` that reaches `min_launches`. Each of `windows` windows
-    replays it back to back (once, or as often as needed for `min_launches` launches),
-    bracketed by HIP events on `stream`; the per-launch time of a window is its span over
-    the launches in it. Each window is followed by one single-replay window, whose
-    excess over per_graph launches is the replay's own overhead (graph submission and the
-    events), reported apart. Returns a dict of medians and the per-window figures."""
+    replays it back to back at least twice (more if `min_launches` asks for it), bracketed
+    by HIP events on `stream`; the per-launch time of a window is its span over the launches
+    in it, so the one replay start it pays is spread over all of them. Each window is
+    followed by one single replay from an idle stream; the window's excess over the single
+    replay is (reps - 1) replays at the pure back-to-back rate, and what the single replay
+    takes beyond per_graph launches at that rate is the replay's own overhead (graph
+    submission and the events), reported apart. Returns a dict of medians and the
+    per-window figures."""
     import bandwidth_bound_decode_amd as bbd
     # One graph holds a whole multiple of the K launches, at least min_launches of them, so
     # that the replay's own cost is spread over as many launches whatever K is.
@@ -164,11 +167,11 @@ def time_windows(torch, launch, per_graph: int, windows: int, min_launches: int,
         with g:
             for i in range(per_graph):
                 launch(i)
-    reps = max(1, math.ceil(min_launches / per_graph))
+    reps = max(2, math.ceil(min_launches / per_graph))
     for _ in range(2):                       # untimed replays
         g.launch(stream)
     torch.cuda.synchronize()
-    per, single = [], []
+    per, single, overhead = [], [], []
     for _ in range(windows):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
@@ -183,13 +186,16 @@ def time_windows(torch, launch, per_graph: int, windows: int, min_launches: int,
         g.launch(stream)
         d.record(stream)
         torch.cuda.synchronize()
-        per.append(a.elapsed_time(b) / 1e3 / (reps * per_graph))
-        single.append(c.elapsed_time(d) / 1e3)
+        span, one = a.elapsed_time(b) / 1e3, c.elapsed_time(d) / 1e3
+        per.append(span / (reps * per_graph))
+        single.append(one)
+        marginal = (span - one) / ((reps - 1) * per_graph)
+        overhead.append(one - per_graph * marginal)
     g.destroy()
     launch_s = statistics.median(per)
     return {"launch_s": launch_s, "per_window_s": per, "windows": windows, "reps": reps,
             "per_graph": per_graph, "timed_launches": windows * reps * per_graph,
-            "replay_overhead_s": statistics.median(single) - per_graph * launch_s,
+            "replay_overhead_s": statistics.median(overhead),
             "spread": (max(per) - min(per)) / launch_s}
 
 
@@ -618,7 +624,8 @@ def main(argv=None):
     ap.add_argument("--windows", type=int, default=7,
                     help="timing windows for the headline (median reported, at least 5)")
     ap.add_argument("--window-launches", type=int, default=200,
-                    help="back-to-back launches per timing window (at least)")
+                    help="launches per graph (at least); each timing window replays the "
+                         "graph twice back to back")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-shapes", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
@@ -693,9 +700,10 @@ def main(argv=None):
                    "rotation_copies": res["rotation_copies"], "plan": plan.info},
         "timing": {"method": "the K steps (one rotated launch each), repeated to a whole "
                              f"multiple of K of at least {args.window_launches} launches, "
-                             "captured in one graph; each window is one replay between two HIP "
-                             "events on the replay stream; value and ms_per_step use the "
-                             "median window",
+                             "captured in one graph; each window is back-to-back replays "
+                             f"({tw['reps']} here) between two HIP events on the replay "
+                             "stream, its span over the launches in it; value and ms_per_step "
+                             "use the median window",
                    "launches_per_graph": tw["per_graph"],
                    "windows": tw["windows"], "launches_per_window": tw["reps"] * tw["per_graph"],
                    "timed_launches": tw["timed_launches"],
@@ -703,9 +711,10 @@ def main(argv=None):
                    "window_spread": round(tw["spread"], 5),
                    "replay_overhead_us": round(tw["replay_overhead_s"] * 1e6, 3),
                    "replay_overhead_note": "one replay of the graph from an idle stream "
-                                           "minus its launches at the back-to-back rate: "
-                                           "graph submission and event cost, paid once per "
-                                           "replay"},
+                                           "minus its launches at the marginal rate of the "
+                                           "window's further replays: graph submission and "
+                                           "event cost, paid once per window (so included "
+                                           "in value, spread over its launches)"},
         "pct_of_peak": round(100 * value_TBps * 1e12 / PEAK_HBM, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved_GBps, 1), "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": round(achieved_GBps * 1e9 / PEAK_HBM, 4),

@@ -71,9 +71,10 @@ typedef struct gemv_plan_s *gemv_plan_t;
  *                   enforced by reserving LDS per workgroup (the kernels use none).
  *   mfma            the matrix-core kernel for batches (decode-GEMV page: past a handful of
  *                   vectors the work stops being a matrix-vector product and matrix units
- *                   start to pay): 0 = automatic (M >= 8 with no tile, split or cap
- *                   forced), 1 = for any M >= 2, -1 = never. It needs K to be a multiple of
- *                   64. It runs only for 16-byte-aligned single-matrix calls; other calls of
+ *                   start to pay; on MI355X they do from M = 2): 0 = automatic (M >= 2
+ *                   with no tile, split or cap forced), 1 = for any M >= 2, -1 = never. It
+ *                   needs K to be a multiple of 64 (of 128 for the 16-row form, M <= 8).
+ *                   It runs only for 16-byte-aligned single-matrix calls; other calls of
  *                   the same plan take the VALU kernels the fields above describe. The
  *                   VALU kernels sum every output in the same order at every M, so with
  *                   -1 each row of a batched result is bitwise equal to its batch-1 result;
@@ -132,12 +133,15 @@ typedef struct {
        fields above then describe the kernels every other call of the plan takes). */
     int mfma;
     int mfma_splits;        /* K slices; > 1 uses the workspace like a VALU split */
-    int64_t mfma_slice;     /* K elements per slice, a multiple of 64 */
-    int mfma_grid_x;        /* 32-row blocks: ceil(N / 32); 8 waves per workgroup */
+    int64_t mfma_slice;     /* K elements per slice, a multiple of the chunk */
+    int mfma_grid_x;        /* row blocks: ceil(N / mfma_rows); 8 waves per workgroup */
     int mfma_depth_bound;   /* h for that kernel, counting 32 roundings per MFMA */
     int weights;            /* the plan's weight format */
     int prologue;           /* the plan's input prologue (0: none) */
     int int4_fp16;          /* INT4: 1 when the workgroups try the fp16 form of staged x */
+    int mfma_rows;          /* rows per matrix-core workgroup: 16 (M <= 8 and K a multiple
+                               of 128; chunks of 128 K elements) or 32 (chunks of 64); 0
+                               without the matrix-core launch */
 } gemv_plan_info;
 
 /*

@@ -1,7 +1,7 @@
 """GPU parity of skinny batches (M = 1..16): within tolerance of the oracle, and, on the VALU
 kernels, every row of Y bitwise equal to the batch-1 run on that row of X (their split count
 and per-row summation order do not depend on M). Plans that take the matrix-core kernel
-(M >= 8 with K a multiple of 64) meet the tolerance in another summation order; the
+(M >= 2 with K a multiple of 64) meet the tolerance in another summation order; the
 invariance is checked on the same inputs with that kernel switched off."""
 import pytest
 import torch

@@ -1,5 +1,6 @@
-"""GPU parity of the matrix-core batch kernel: within tolerance of the oracle at the
-down_proj shape and on small shapes that span several 32-row blocks with a ragged last one,
+"""GPU parity of the matrix-core batch kernel (both forms: 16-row blocks for M <= 8, 32-row
+blocks otherwise): within tolerance of the oracle at the down_proj shape and on small shapes
+that span several row blocks with a ragged last one,
 unsplit and split over K; exact where every partial sum is exact (identity, one-hot, constant
 W); reproducible bit for bit; and the unaligned fallback equal to the VALU plan."""
 import numpy as np
@@ -12,12 +13,15 @@ from gpu_helpers import bits_equal, device_matrix, draw, gemv, oracle_check
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("m", [8, 12])
+@pytest.mark.parametrize("m", [8, 12, 16])
 def test_down_proj_batches(m):
+    """Full size: M = 8 on the 16-row form (unsplit), M = 12 and 16 on the 32-row form (two
+    slices and the combine)."""
     w, x = draw(4096, 14336, m, seed=300 + m)
     W, X = device_matrix(w), device_matrix(x)
     Y, p = gemv(W, X)
-    assert p.info["mfma"] == 1 and p.info["mfma_splits"] == 2, p.info
+    want = (16, 1) if m <= 8 else (32, 2)
+    assert p.info["mfma"] == 1 and (p.info["mfma_rows"], p.info["mfma_splits"]) == want, p.info
     oracle_check(W, X, Y, f"mfma down m={m}")
     Y2, _ = gemv(W, X, plan=p)
     assert bits_equal(Y, Y2), "not reproducible"
@@ -37,16 +41,19 @@ def test_shapes_every_batch(n, k):
         assert bits_equal(Y, Y2), f"n={n} k={k} m={m} not reproducible"
 
 
-def test_identity_and_one_hot_exact():
+@pytest.mark.parametrize("m", [16, 8])
+def test_identity_and_one_hot_exact(m):
     n = k = 512
-    _, x = draw(1, k, 16, seed=7)
+    _, x = draw(1, k, m, seed=7)
     eye = torch.eye(n, dtype=torch.bfloat16)
     Y, p = gemv(device_matrix(eye), device_matrix(x), mfma=1)
-    assert p.info["mfma"] == 1
+    assert p.info["mfma"] == 1 and p.info["mfma_rows"] == (16 if m <= 8 else 32)
     assert bits_equal(Y, x.float()), "W = I must return X exactly"
     w, _ = draw(300, 4096, 1, seed=8)
     cols = [0, 1, 31, 32, 63, 64, 511, 512, 2047, 2048, 4032, 4095, 7, 100, 3000, 4094]
-    xo = torch.zeros(16, 4096, dtype=torch.bfloat16)
+    if m <= 8:   # both lines, every MFMA and piece of a 128-element chunk, and slice edges
+        cols = [0, 33, 71, 127, 128, 1023, 2050, 4095]
+    xo = torch.zeros(m, 4096, dtype=torch.bfloat16)
     for i, c in enumerate(cols):
         xo[i, c] = 1.0
     Y, p = gemv(device_matrix(w), device_matrix(xo), mfma=1)
@@ -82,8 +89,9 @@ def test_accumulator_rounded_once_per_mfma():
     assert bits_equal(Y, torch.full((m, n), 1.0 + 2.0 ** -20)), Y[0, :4].tolist()
 
 
-def test_special_values():
-    n, k, m = 64, 1024, 9
+@pytest.mark.parametrize("m", [9, 8])
+def test_special_values(m):
+    n, k = 64, 1024
     w, x = draw(n, k, m, seed=10)
     w[3, 17] = float("inf")
     w[5, 900] = float("nan")
@@ -92,6 +100,19 @@ def test_special_values():
     assert torch.isinf(Y[:, 3]).all() and torch.isnan(Y[:, 5]).all()
     keep = [i for i in range(n) if i not in (3, 5)]
     assert torch.isfinite(Y[:, keep]).all()
+
+
+def test_accumulator_rounded_once_per_mfma_narrow():
+    """The same pin on the 16-row form: K = 128 is one chunk, four MFMAs in order on one
+    wave; the first gives exactly 1.0 and each later one adds 32 products of 2^-25."""
+    n, k, m = 16, 128, 8
+    w = torch.zeros(n, k, dtype=torch.bfloat16)
+    w[:, 0] = 1.0
+    w[:, 32:] = 2.0 ** -25
+    x = torch.ones(m, k, dtype=torch.bfloat16)
+    Y, p = gemv(device_matrix(w), device_matrix(x), mfma=1)
+    assert (p.info["mfma_rows"], p.info["mfma_splits"]) == (16, 1), p.info
+    assert bits_equal(Y, torch.full((m, n), 1.0 + 3 * 2.0 ** -20)), Y[0, :4].tolist()
 
 
 def test_unaligned_call_takes_the_valu_kernels():

@@ -77,13 +77,18 @@ def test_mi355x_plans(n, k, m):
     else:
         assert p.workspace_size == 0
     if info["mfma"]:
-        ms, msl = info["mfma_splits"], info["mfma_slice"]
-        assert m >= 8 and k % 64 == 0 and msl % 64 == 0
+        ms, msl, rows = info["mfma_splits"], info["mfma_slice"], info["mfma_rows"]
+        # 16-row blocks with 128-element chunks for M <= 8, else 32-row with 64-element ones
+        assert rows == (16 if m <= 8 and k % 128 == 0 else 32)
+        chunk = 128 if rows == 16 else 64
+        assert m >= 2 and k % chunk == 0 and msl % chunk == 0
         assert (ms - 1) * msl < k <= ms * msl
-        assert info["mfma_grid_x"] == math.ceil(n / 32)
+        assert info["mfma_grid_x"] == math.ceil(n / rows)
         assert info["mfma_depth_bound"] <= 160
         # one 8-wave workgroup per CU at least, or no split because the rows cover them
-        assert info["mfma_grid_x"] * ms >= 256 or ms == k // 512
+        assert info["mfma_grid_x"] * ms >= 256 or ms == k // (8 * chunk)
+    else:
+        assert info["mfma_rows"] == 0
     # the tolerance 1e-5 * sum|terms| is guaranteed: gamma_h < 1e-5 for h <= 160
     assert info["depth_bound"] <= 160
     h = info["depth_bound"]
@@ -217,15 +222,25 @@ def test_plan_search_terminates_for_any_shape():
 
 
 def test_mfma_plans():
-    """The matrix-core launch: chosen from M = 8 with no tile option forced, split over K
-    only while 32-row blocks leave CUs without one, and its partials fit the workspace."""
+    """The matrix-core launch: chosen from M = 2 with no tile option forced, split over K
+    only while its row blocks leave CUs without one, and its partials fit the workspace."""
     i = plan(4096, 14336, 16).info
     assert (i["mfma"], i["mfma_splits"], i["mfma_grid_x"], i["mfma_slice"]) == (1, 2, 128, 7168)
     # 32 roundings in the first MFMA, 2 per later chunk of the wave's 14, 7 wave adds, 1 combine
     assert i["mfma_depth_bound"] == 32 + 2 * 14 + 7 + 1
     assert plan(4096, 14336, 16).workspace_size == 4 * 4096 + 2 * 16 * 4096 * 4
-    assert plan(4096, 14336, 8).info["mfma"] == 1
-    assert plan(4096, 14336, 7).info["mfma"] == 0
+    assert i["mfma_rows"] == 32
+    # M <= 8: 16-row blocks and 128-element chunks, so 4096 rows fill 256 CUs unsplit;
+    # 4 MFMAs per chunk of the wave's 14
+    e = plan(4096, 14336, 8).info
+    assert (e["mfma"], e["mfma_rows"], e["mfma_splits"], e["mfma_grid_x"], e["mfma_slice"]) == \
+        (1, 16, 1, 256, 14336)
+    assert e["mfma_depth_bound"] == 32 + 4 * 14 + 7
+    assert plan(4096, 14336, 8).workspace_size == 0
+    assert plan(4096, 4160, 8).info["mfma_rows"] == 32     # K not a multiple of 128
+    assert plan(4096, 14336, 9).info["mfma_rows"] == 32
+    assert plan(4096, 14336, 2).info["mfma"] == 1           # the default from M = 2
+    assert plan(4096, 14336, 2).info["mfma_rows"] == 16
     assert plan(4096, 14336, 16, mfma=-1).info["mfma"] == 0
     assert plan(4096, 14336, 16, mfma=-1).workspace_size == 0
     assert plan(4096, 14336, 2, mfma=1).info["mfma"] == 1
@@ -240,6 +255,9 @@ def test_mfma_plans():
     assert plan(28672, 4096, 16).workspace_size == 0
     small = plan(33, 4096, 9).info                            # 2 blocks: split to the cap
     assert small["mfma_splits"] == 4096 // 512 and small["mfma_slice"] == 512
+    small8 = plan(33, 4096, 8).info                           # 3 narrow blocks: the same
+    assert small8["mfma_rows"] == 16 and small8["mfma_grid_x"] == 3
+    assert small8["mfma_splits"] == 4096 // 1024 and small8["mfma_slice"] == 1024
     long_k = plan(64, 1 << 19, 16).info                       # accuracy forces the split
     assert long_k["mfma"] == 1 and long_k["mfma_depth_bound"] <= 160
     with pytest.raises(bbd.GemvError):
