@@ -510,7 +510,14 @@ __global__ void __launch_bounds__(512) gemv_unaligned(ArgsT<MULTI> p)
 // kernels read x. When the M rows do not fit, they are staged `chunk` vectors at a time,
 // with a barrier between chunks. Each lane takes vectors l, l + 64, ... in increasing order
 // and then the head and tail elements, as gemv_unaligned does, so both give bitwise the
-// same result.
+// same result on those rows.
+// The rows of a class past its last whole group of 8 (at most 7, the tail rows) are summed
+// differently: all 8 waves of one workgroup share each such row, wave w taking the w-th
+// eighth of its vectors and reading x from global memory, and the 8 wave sums are added in
+// wave order. A lone leftover row (4097 rows in 8 classes leave one) then costs an eighth
+// of a pass instead of a whole extra pass for one workgroup (measured at 4097 x 14337:
+// 26.3 us against 22.8 us at 4096 rows). Which rows are tail rows depends only on N and the
+// classes, and their order on nothing but K, so every M sums each row the same way.
 // Two shapes of wave: R rows per wave, U vectors per lane and row per burst (the same bytes
 // in flight). One row per wave spreads the rows over more waves; two rows per wave halve
 // the LDS reads of x, which at larger M bound the kernel.
@@ -518,6 +525,10 @@ struct ShiftShape {
     int r, u;
 };
 constexpr ShiftShape kShiftShapes[2] = {{1, 4}, {2, 2}};
+// One row per wave up to M = 4, two above (measured at 4097 x 14337, M = 1..16).
+constexpr int shift_shape_of(int m) { return m <= 4 ? 0 : 1; }
+constexpr int kTailGroup = 8;   // tail rows: those past the last whole group of this many
+constexpr int kShiftWaves = 8;  // waves per workgroup of the class-staged kernel
 
 template <int M, int R, int U>
 __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes, int chunk)
@@ -529,8 +540,11 @@ __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes, i
     const int waves = (int)(blockDim.x >> 6);
     const int cls = blockIdx.y;
     const int class_rows = (p.n - cls + classes - 1) / classes;
-    const int blocks = (class_rows + waves * R - 1) / (waves * R);   // row blocks of the class
-    if ((int)blockIdx.x >= blocks)   // uniform per workgroup
+    const int tail0 = class_rows & ~(kTailGroup - 1);   // rows [tail0, class_rows): tail rows
+    const int ntail = class_rows - tail0;
+    const int blocks = (tail0 + waves * R - 1) / (waves * R);   // row blocks of the rest
+    const bool has_main = (int)blockIdx.x < blocks;   // uniform per workgroup
+    if (!has_main && (int)blockIdx.x >= ntail)
         return;
     const uint16_t *w_cls = p.w0 + (int64_t)cls * p.ldw0;
     const int h = (int)((8u - (unsigned)(((uintptr_t)w_cls >> 1) & 7u)) & 7u);
@@ -618,114 +632,176 @@ __global__ void __launch_bounds__(512) gemv_unaligned_lds(Args p, int classes, i
             for (int r = 0; r < R; ++r)
                 wv[u][r] = load_stream(wr[r] + 8 * min(s0 + lane + 64 * u, nvec - 1));
     };
-    auto rows_of = [&](int blk) {   // rows past the class re-read its last row, unstored
+    auto rows_of = [&](int blk) {   // rows past tail0 re-read row tail0 - 1, unstored
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int j = min((blk * waves + wave) * R + r, class_rows - 1);
+            const int j = min((blk * waves + wave) * R + r, tail0 - 1);
             wr[r] = p.w0 + (int64_t)(cls + classes * j) * p.ldw0 + ka;
         }
     };
 
+    // Tail rows first: workgroup b takes tail rows b, b + gridDim.x, ... of its class. They
+    // read x from global memory, so their latency overlaps the other workgroups' streams
+    // and this workgroup's own x staging instead of trailing its last row block.
+    constexpr int kTailU = M <= 4 ? 4 : 2;   // vectors per lane in flight on a tail row
+    const int per = (nvec + waves - 1) / waves;
+    const int vb = wave * per, ve = min(nvec, vb + per);   // this wave's vectors of the row
+    __shared__ float sums[kShiftWaves * M];                // [wave][m]
+    for (int t = blockIdx.x; t < ntail; t += gridDim.x) {
+        const int j = tail0 + t;
+        const uint16_t *wrow = p.w0 + (int64_t)(cls + classes * j) * p.ldw0 + ka;
+        float acc[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            acc[m] = 0.f;
+        for (int v0 = vb; v0 < ve; v0 += 64 * kTailU) {
+            u32x4 tw[kTailU];
+#pragma unroll
+            for (int u = 0; u < kTailU; ++u)
+                tw[u] = load_stream(wrow + 8 * min(v0 + lane + 64 * u, ve - 1));
+#pragma unroll
+            for (int u = 0; u < kTailU; ++u) {
+                const int v = v0 + lane + 64 * u;
+                const int vc = min(v, ve - 1);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const u32x4 xv = x_window(p.x + (int64_t)m * p.ldx, ka + 8 * vc, p.k, q[m]);
+                    const float next = dot8(tw[u], xv, acc[m]);
+                    acc[m] = v < ve ? next : acc[m];
+                }
+            }
+        }
+        if (wave == 0) {   // lanes 0..7 the head elements, lanes 8..15 the tail elements
+            const int kk = lane < 8 ? lane : tail_begin + (lane - 8);
+            const bool take = lane < 8 ? kk < ka : (lane < 16 && kk < p.k);
+            if (take) {
+                const float w = bf16_to_f32(wrow[kk - ka]);
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    acc[m] = fmaf(w, bf16_to_f32(p.x[(int64_t)m * p.ldx + kk]), acc[m]);
+            }
+        }
+        float ws[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            ws[m] = lane63(wave_sum(acc[m]));
+        __syncthreads();   // the previous tail row's sums have been read
+        if (lane == 0) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                sums[wave * M + m] = ws[m];
+        }
+        __syncthreads();
+        if (wave == 0 && lane < M) {
+            float v = sums[lane];
+            for (int w = 1; w < waves; ++w)
+                v += sums[w * M + lane];
+            p.y0[(int64_t)lane * p.ldy0 + cls + classes * j] = v;
+        }
+    }
+
     // When the M rows of x fit (chunk >= nvec) they are staged once and serve every row
     // block this workgroup takes; otherwise each row block stages them chunk by chunk.
     const bool once = chunk >= nvec;
-    rows_of(blockIdx.x);
-    if (once) {
-        stage(0, nvec, [&] {
-            if (nvec > 0)
-                burst(0);   // the first weights are in flight while x is staged
-        });
-        __syncthreads();
-    } else if (nvec > 0) {
-        burst(0);
-    }
-    for (int blk = blockIdx.x;;) {
-        float acc[R][M];
+    if (has_main) {
+        rows_of(blockIdx.x);
+        if (once) {
+            stage(0, nvec, [&] {
+                if (nvec > 0)
+                    burst(0);   // the first weights are in flight while x is staged
+            });
+            __syncthreads();
+        } else if (nvec > 0) {
+            burst(0);
+        }
+        for (int blk = blockIdx.x;;) {
+            float acc[R][M];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int m = 0; m < M; ++m)
-                acc[r][m] = 0.f;
-        // chunk is a multiple of 64 * U (or covers the row), so every lane still meets its
-        // vectors l, l + 64, ... in increasing order, whatever the chunking.
-        for (int c0 = 0; c0 < nvec; c0 += chunk) {
-            const int c1 = min(nvec, c0 + chunk);
-            if (!once) {
-                // Chunks: the burst goes out before the barrier, while other waves finish
-                // the previous chunk (measured faster here than after the first x loads).
-                if (c0 > 0)
-                    burst(c0);
-                __syncthreads();   // every wave is done with the previous contents
-                stage(c0, c1, [] {});
-                __syncthreads();
-            }
-            for (int s0 = c0; s0 < c1; s0 += 64 * U) {
-                if (s0 > c0)
-                    burst(s0);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int m = 0; m < M; ++m)
+                    acc[r][m] = 0.f;
+            // chunk is a multiple of 64 * U (or covers the row), so every lane still meets its
+            // vectors l, l + 64, ... in increasing order, whatever the chunking.
+            for (int c0 = 0; c0 < nvec; c0 += chunk) {
+                const int c1 = min(nvec, c0 + chunk);
+                if (!once) {
+                    // Chunks: the burst goes out before the barrier, while other waves finish
+                    // the previous chunk (measured faster here than after the first x loads).
+                    if (c0 > 0)
+                        burst(c0);
+                    __syncthreads();   // every wave is done with the previous contents
+                    stage(c0, c1, [] {});
+                    __syncthreads();
+                }
+                for (int s0 = c0; s0 < c1; s0 += 64 * U) {
+                    if (s0 > c0)
+                        burst(s0);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int v = s0 + lane + 64 * u;
-                    const int vc = min(v, c1 - 1);
+                    for (int u = 0; u < U; ++u) {
+                        const int v = s0 + lane + 64 * u;
+                        const int vc = min(v, c1 - 1);
 #pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        const u32x4 xv = xs[m * chunk + vc - c0];
+                        for (int m = 0; m < M; ++m) {
+                            const u32x4 xv = xs[m * chunk + vc - c0];
 #pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            const float next = dot8(wv[u][r], xv, acc[r][m]);
-                            acc[r][m] = v < c1 ? next : acc[r][m];
+                            for (int r = 0; r < R; ++r) {
+                                const float next = dot8(wv[u][r], xv, acc[r][m]);
+                                acc[r][m] = v < c1 ? next : acc[r][m];
+                            }
                         }
                     }
                 }
             }
-        }
-        // Lanes 0..7 take the head elements, lanes 8..15 the tail elements.
-        const int kk = lane < 8 ? lane : tail_begin + (lane - 8);
-        const bool take = lane < 8 ? kk < ka : (lane < 16 && kk < p.k);
-        if (take) {
+            // Lanes 0..7 take the head elements, lanes 8..15 the tail elements.
+            const int kk = lane < 8 ? lane : tail_begin + (lane - 8);
+            const bool take = lane < 8 ? kk < ka : (lane < 16 && kk < p.k);
+            if (take) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float w = bf16_to_f32(wr[r][kk - ka]);
+                for (int r = 0; r < R; ++r) {
+                    const float w = bf16_to_f32(wr[r][kk - ka]);
 #pragma unroll
-                for (int m = 0; m < M; ++m)
-                    acc[r][m] = fmaf(w, bf16_to_f32(p.x[(int64_t)m * p.ldx + kk]), acc[r][m]);
+                    for (int m = 0; m < M; ++m)
+                        acc[r][m] = fmaf(w, bf16_to_f32(p.x[(int64_t)m * p.ldx + kk]), acc[r][m]);
+                }
             }
-        }
-        float out = 0.f;
+            float out = 0.f;
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const float sum = lane63(wave_sum(acc[r][m]));
-                if (lane == r * M + m)
-                    out = sum;
+                for (int m = 0; m < M; ++m) {
+                    const float sum = lane63(wave_sum(acc[r][m]));
+                    if (lane == r * M + m)
+                        out = sum;
+                }
+            const int j0 = (blk * waves + wave) * R;
+            if (lane < R * M) {
+                const int r = lane / M, m = lane - (lane / M) * M;
+                if (j0 + r < tail0)
+                    p.y0[(int64_t)m * p.ldy0 + cls + classes * (j0 + r)] = out;
             }
-        const int j0 = (blk * waves + wave) * R;
-        if (lane < R * M) {
-            const int r = lane / M, m = lane - (lane / M) * M;
-            if (j0 + r < class_rows)
-                p.y0[(int64_t)m * p.ldy0 + cls + classes * (j0 + r)] = out;
+            blk += gridDim.x;
+            if (blk >= blocks)
+                break;
+            rows_of(blk);
+            if (nvec > 0)
+                burst(0);
         }
-        blk += gridDim.x;
-        if (blk >= blocks)
-            break;
-        rows_of(blk);
-        if (nvec > 0)
-            burst(0);
     }
 }
 
-template <int S, size_t... I>
+template <size_t... I>
 std::array<const void *, GEMV_MAX_M> unaligned_lds_table(std::index_sequence<I...>)
 {
     return {reinterpret_cast<const void *>(
-        &gemv_unaligned_lds<(int)I + 1, kShiftShapes[S].r, kShiftShapes[S].u>)...};
+        &gemv_unaligned_lds<(int)I + 1, kShiftShapes[shift_shape_of((int)I + 1)].r,
+                            kShiftShapes[shift_shape_of((int)I + 1)].u>)...};
 }
 
-// [shape][M - 1]
-const std::array<const void *, GEMV_MAX_M> kUnalignedLds[2] = {
-    unaligned_lds_table<0>(std::make_index_sequence<GEMV_MAX_M>{}),
-    unaligned_lds_table<1>(std::make_index_sequence<GEMV_MAX_M>{})};
+// [M - 1], each M on its wave shape
+const std::array<const void *, GEMV_MAX_M> kUnalignedLds =
+    unaligned_lds_table(std::make_index_sequence<GEMV_MAX_M>{});
 
 // ---------------------------------------------------------------------------- dispatch
 // Kernel handles for hipLaunchKernel; fused instances take ArgsMulti, the others Args.
@@ -789,8 +865,7 @@ gemv_status launch_unaligned_lds(gemv_plan_t p, const gemv_segment &seg, const v
     if (p->splits != 1 || vecs == 0)
         return GEMV_OK;
     const int64_t per_vec = (int64_t)p->m * (int64_t)sizeof(u32x4);
-    // One row per wave up to M = 4, two above (measured at 4097 x 14337, M = 1..16).
-    const int shape = p->m <= 4 ? 0 : 1;
+    const int shape = shift_shape_of(p->m);
     const ShiftShape sh = kShiftShapes[shape];
     const int64_t burst = (int64_t)kWaveLanes * sh.u;
     int64_t chunk_vecs = vecs;
@@ -800,7 +875,7 @@ gemv_status launch_unaligned_lds(gemv_plan_t p, const gemv_segment &seg, const v
         return GEMV_OK;
     int chunk = (int)chunk_vecs;
     const size_t bytes = (size_t)(chunk_vecs * per_vec);
-    const void *fn = kUnalignedLds[shape][p->m - 1];
+    const void *fn = kUnalignedLds[p->m - 1];
     static std::atomic<bool> allowed[2][GEMV_MAX_M + 1];
     if (bytes > 64 * 1024 && !allowed[shape][p->m].load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -819,9 +894,15 @@ gemv_status launch_unaligned_lds(gemv_plan_t p, const gemv_segment &seg, const v
         classes = 2;
     else if (g % 2 == 0)
         classes = 4;
-    const int waves = 8;
+    const int waves = kShiftWaves;
+    // Row blocks of whole groups of kTailGroup rows in the largest class, and the most tail
+    // rows any class has (each needs a workgroup of its class).
     const int64_t class_rows = (p->n + classes - 1) / classes;
-    int64_t blocks = (class_rows + (int64_t)sh.r * waves - 1) / ((int64_t)sh.r * waves);
+    const int64_t main_rows = class_rows / kTailGroup * kTailGroup;
+    int64_t blocks = (main_rows + (int64_t)sh.r * waves - 1) / ((int64_t)sh.r * waves);
+    int64_t tails = 0;
+    for (int c = 0; c < classes; ++c)
+        tails = std::max<int64_t>(tails, ((p->n - c + classes - 1) / classes) % kTailGroup);
     // When x fits, workgroups take row blocks blockIdx.x, + gridDim.x, ...: no more of them
     // per class than the classes' share of what the device holds at once, so none waits for
     // a slot and x is staged once per workgroup. Chunked x is staged per row block anyway,
@@ -845,6 +926,9 @@ gemv_status launch_unaligned_lds(gemv_plan_t p, const gemv_segment &seg, const v
         const int64_t resident = (int64_t)std::max(per_cu, 1) * p->dev.compute_units;
         blocks = std::min(blocks, std::max<int64_t>(1, (resident + classes - 1) / classes));
     }
+    blocks = std::max(blocks, tails);
+    if (blocks < 1)
+        blocks = 1;
     Args a;
     memset(&a, 0, sizeof a);
     a.w0 = static_cast<const uint16_t *>(seg.W);
