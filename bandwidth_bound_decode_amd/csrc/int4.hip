@@ -13,20 +13,19 @@
 // vector-memory path carries weights and scales only: x is 4 bytes per packed weight byte,
 // and loading it per wave measured up to 1.5x slower (probe sweep at the Llama shapes).
 // Per 32-bit word (8 weights):
-//   - (word << 4) & 0xF0F0F0F0 puts the even-indexed nibbles, and word & 0xF0F0F0F0 the
-//     odd-indexed ones, in the top half of a byte each; read as a signed byte that is 16 v,
-//     exactly;
-//   - each signed byte converts to fp32 (one instruction with a byte select), and the top
-//     halves of two such floats are the bf16 pair (16 v_2i, 16 v_2i+1), exactly, which
-//     v_dot2c_f32_bf16 multiplies by the x pair (x_2i, x_2i+1);
-// so the 32 products of a vector form one fp32 chain, p = sum 16 v x, and the group scale
-// then enters once: acc = fma(p, scale / 16, acc). No product is formed inexactly (16 v has
-// 4 significant bits, x 8) and no offset is subtracted after the fact, so the error analysis
-// of the bf16 path carries over unchanged.
+//   - v_cvt_off_f32_i4 turns the signed nibble in bits 3:0 of its operand into v / 16 in
+//     fp32, exactly; with a byte select it reads the even-indexed nibbles straight from the
+//     word's bytes, and from the word shifted right by 4 the odd-indexed ones;
+//   - the top halves of two such floats are the bf16 pair (v_2i / 16, v_2i+1 / 16), exactly,
+//     which v_dot2c_f32_bf16 multiplies by the x pair (x_2i, x_2i+1);
+// so the 32 products of a vector form one fp32 chain, p = sum (v / 16) x, and the group
+// scale then enters once: acc = fma(p, 16 scale, acc). No product is formed inexactly (v / 16
+// has 4 significant bits, x 8) and no offset is subtracted after the fact, so the error
+// analysis of the bf16 path carries over unchanged.
 //
-// That unpack costs 18 VALU instructions per 8 weights, which at the HBM rate is most of a
-// CU's VALU issue. When x is staged in LDS the kernel first tries a cheaper exact form (13
-// per 8 weights) built on fp16:
+// That unpack costs 17 VALU instructions per 8 weights (one shift, 8 conversions, 4 packs,
+// 4 dot products), which at the HBM rate is most of a CU's VALU issue. When x is staged in
+// LDS the kernel first tries a cheaper exact form (13 per 8 weights) built on fp16:
 //   - x is staged per 32-element vector as fp16 x * 2^s, with s chosen per vector so that
 //     its largest magnitude lands in [2^15, 2^16); the 2^-s goes into that vector's scale
 //     multiplier. The conversion works on the bit patterns (exponent rebased by a packed
@@ -57,25 +56,36 @@ namespace {
 
 using namespace bbd;
 
-// bf16 pair (16 v_2i, 16 v_2i+1) for pair i of a packed word, from its even/odd bytes.
+// bf16 pair (v_2i / 16, v_2i+1 / 16) for pair i of a packed word d, t = d >> 4. Byte i of d
+// holds element 2i in its low nibble and byte i of t element 2i + 1: bit-field extracts of
+// bytes fold into the conversions' byte selects.
 template <int I>
-__device__ __forceinline__ unsigned int4_pair(unsigned even, unsigned odd)
+__device__ __forceinline__ unsigned int4_pair(unsigned d, unsigned t)
 {
-    const float lo = (float)(int8_t)(even >> (8 * I));
-    const float hi = (float)(int8_t)(odd >> (8 * I));
+    const float lo = __builtin_amdgcn_cvt_off_f32_i4(__builtin_amdgcn_ubfe(d, 8 * I, 8));
+    const float hi = __builtin_amdgcn_cvt_off_f32_i4(__builtin_amdgcn_ubfe(t, 8 * I, 8));
     return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
-// p + sum of the 8 products of packed word d with the x vector half xd (4 bf16 pairs).
+// d >> 4 as a value of its own. Written plainly, the compiler folds the shift into each odd
+// element's extract (a shift per element instead of a byte select on one shifted word).
+__device__ __forceinline__ unsigned shifted_by_4(unsigned d)
+{
+    unsigned t;
+    asm("v_lshrrev_b32 %0, 4, %1" : "=v"(t) : "v"(d));
+    return t;
+}
+
+// p + sum of the 8 products (v / 16) x of packed word d with the x vector half xd (4 bf16
+// pairs).
 __device__ __forceinline__ float int4_dot8(unsigned d, u32x4 xd, float p)
 {
-    const unsigned even = (d << 4) & 0xF0F0F0F0u;
-    const unsigned odd = d & 0xF0F0F0F0u;
+    const unsigned t = shifted_by_4(d);
     const unsigned x0 = xd.x, x1 = xd.y, x2 = xd.z, x3 = xd.w;
-    p = dot2(int4_pair<0>(even, odd), x0, p);
-    p = dot2(int4_pair<1>(even, odd), x1, p);
-    p = dot2(int4_pair<2>(even, odd), x2, p);
-    p = dot2(int4_pair<3>(even, odd), x3, p);
+    p = dot2(int4_pair<0>(d, t), x0, p);
+    p = dot2(int4_pair<1>(d, t), x1, p);
+    p = dot2(int4_pair<2>(d, t), x2, p);
+    p = dot2(int4_pair<3>(d, t), x3, p);
     return p;
 }
 
@@ -219,7 +229,7 @@ __device__ __forceinline__ void use_burst(const Burst<U, R, XLDS> &b, const unsi
                 p = int4_dot8(w1, xv[1], p);
                 p = int4_dot8(w2, xv[2], p);
                 p = int4_dot8(w3, xv[3], p);
-                scale = bf16_to_f32(b.s[u][r]) * 0.0625f;   // exact: a power of two
+                scale = bf16_to_f32(b.s[u][r]) * 16.f;   // exact: a power of two
             }
             const float next = fmaf(p, scale, acc[r]);
             acc[r] = in ? next : acc[r];

@@ -149,15 +149,13 @@ def time_windows(torch, launch, per_graph: int, windows: int, min_launches: int,
     """Per-launch time of `launch` run back to back, independent of the graph size.
 
     The launches are captured into one graph on `stream`: `per_graph` of them, repeated to a
-    whole multiple of `per_graph` that reaches `min_launches`. Each of `windows` windows
-    replays it back to back at least twice (more if `min_launches` asks for it), bracketed
-    by HIP events on `stream`; the per-launch time of a window is its span over the launches
-    in it, so the one replay start it pays is spread over all of them. Each window is
-    followed by one single replay from an idle stream; the window's excess over the single
-    replay is (reps - 1) replays at the pure back-to-back rate, and what the single replay
-    takes beyond per_graph launches at that rate is the replay's own overhead (graph
-    submission and the events), reported apart. Returns a dict of medians and the
-    per-window figures."""
+    whole multiple of `per_graph` that reaches `min_launches`. Each of `windows` windows is
+    an untimed leading replay, then two replays back to back (more if `min_launches` asks
+    for it) bracketed by HIP events on `stream`: while the GPU runs the leading replay the
+    host has already queued the timed ones, so the window holds the launches and none of the
+    host's submission latency (which an idle GPU would wait for, see replay_cost). The
+    per-launch time of a window is its span over the launches in it. Returns a dict of
+    medians and the per-window figures."""
     import bandwidth_bound_decode_amd as bbd
     # One graph holds a whole multiple of the K launches, at least min_launches of them, so
     # that the replay's own cost is spread over as many launches whatever K is.
@@ -171,32 +169,52 @@ def time_windows(torch, launch, per_graph: int, windows: int, min_launches: int,
     for _ in range(2):                       # untimed replays
         g.launch(stream)
     torch.cuda.synchronize()
-    per, single, overhead = [], [], []
+    per = []
     for _ in range(windows):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
-        c = torch.cuda.Event(enable_timing=True)
-        d = torch.cuda.Event(enable_timing=True)
+        g.launch(stream)                     # leading replay, untimed
         a.record(stream)
         for _ in range(reps):
             g.launch(stream)
         b.record(stream)
         torch.cuda.synchronize()
-        c.record(stream)                     # one replay from an idle stream, as a lone step
-        g.launch(stream)
-        d.record(stream)
-        torch.cuda.synchronize()
-        span, one = a.elapsed_time(b) / 1e3, c.elapsed_time(d) / 1e3
-        per.append(span / (reps * per_graph))
-        single.append(one)
-        marginal = (span - one) / ((reps - 1) * per_graph)
-        overhead.append(one - per_graph * marginal)
+        per.append(a.elapsed_time(b) / 1e3 / (reps * per_graph))
     g.destroy()
     launch_s = statistics.median(per)
     return {"launch_s": launch_s, "per_window_s": per, "windows": windows, "reps": reps,
             "per_graph": per_graph, "timed_launches": windows * reps * per_graph,
-            "replay_overhead_s": statistics.median(overhead),
             "spread": (max(per) - min(per)) / launch_s}
+
+
+def replay_cost(torch, bbd, stream, replays: int = 11) -> float:
+    """Seconds one replay of a graph holding a single tiny GEMV launch (1 x 512) takes
+    between two events on an idle stream, median of `replays`: the host's submission of the
+    replay, the events and one near-empty kernel. What a timing window would pay once if it
+    started on an idle GPU; time_windows starts its windows behind a leading replay instead."""
+    w = torch.zeros((1, 512), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((1, 512), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((1, 1), dtype=torch.float32, device="cuda")
+    plan = bbd.Plan(1, 512, 1)
+    ws = plan.alloc_workspace()
+    g = bbd.Graph(stream)
+    with torch.cuda.stream(stream):
+        with g:
+            bbd.run(plan, w, x, y, ws, stream)
+    for _ in range(2):
+        g.launch(stream)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(replays):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.launch(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / 1e3)
+    g.destroy()
+    return statistics.median(ts)
 
 
 def rotation_arena(torch, w, min_bytes=ROTATION_BYTES):
@@ -247,7 +265,6 @@ def bench_gemv(torch, bbd, g, w, x, steps, warmup, segments=(), windows=5, min_l
            "us_per_launch": t * 1e6, "TBps": nb / t / 1e12, "pct_peak": 100 * nb / t / PEAK_HBM,
            "windows": tw["windows"], "launches_per_window": tw["reps"] * tw["per_graph"],
            "window_spread": tw["spread"],
-           "replay_overhead_us": tw["replay_overhead_s"] * 1e6,
            "isolated_launch_us_median": statistics.median(per) * 1e6,
            "isolated_launch_us_p10": pct(per, 0.1) * 1e6,
            "isolated_launch_us_p90": pct(per, 0.9) * 1e6}
@@ -625,7 +642,7 @@ def main(argv=None):
                     help="timing windows for the headline (median reported, at least 5)")
     ap.add_argument("--window-launches", type=int, default=200,
                     help="launches per graph (at least); each timing window replays the "
-                         "graph twice back to back")
+                         "graph twice back to back behind an untimed leading replay")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-shapes", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
@@ -673,10 +690,11 @@ def main(argv=None):
     launch_s = tw["launch_s"]                 # median over the windows, back to back
     value_TBps = nb / launch_s / 1e12
     achieved_GBps = nb / launch_s / 1e9
+    replay_s = replay_cost(torch, bbd, torch.cuda.Stream())
     log(f"down 4096x14336: {launch_s * 1e6:.3f} us per launch back to back (median of "
         f"{tw['windows']} windows of {tw['reps'] * tw['per_graph']} launches, spread "
-        f"{100 * tw['spread']:.2f} %), {value_TBps:.3f} TB/s; replay overhead "
-        f"{tw['replay_overhead_s'] * 1e6:.1f} us; isolated launches "
+        f"{100 * tw['spread']:.2f} %), {value_TBps:.3f} TB/s; a one-launch graph replay "
+        f"{replay_s * 1e6:.1f} us; isolated launches "
         f"{res['isolated_launch_us_median']:.2f} us; plan {plan.info}")
     traffic, traffic_note = counter_traffic(plan.info)
 
@@ -700,21 +718,22 @@ def main(argv=None):
                    "rotation_copies": res["rotation_copies"], "plan": plan.info},
         "timing": {"method": "the K steps (one rotated launch each), repeated to a whole "
                              f"multiple of K of at least {args.window_launches} launches, "
-                             "captured in one graph; each window is back-to-back replays "
-                             f"({tw['reps']} here) between two HIP events on the replay "
-                             "stream, its span over the launches in it; value and ms_per_step "
-                             "use the median window",
+                             "captured in one graph; each window is an untimed leading replay "
+                             f"and then {tw['reps']} back-to-back replays between two HIP "
+                             "events on the replay stream, its span over the launches in it; "
+                             "value and ms_per_step use the median window",
                    "launches_per_graph": tw["per_graph"],
                    "windows": tw["windows"], "launches_per_window": tw["reps"] * tw["per_graph"],
                    "timed_launches": tw["timed_launches"],
                    "per_window_us": [round(t * 1e6, 4) for t in tw["per_window_s"]],
                    "window_spread": round(tw["spread"], 5),
-                   "replay_overhead_us": round(tw["replay_overhead_s"] * 1e6, 3),
-                   "replay_overhead_note": "one replay of the graph from an idle stream "
-                                           "minus its launches at the marginal rate of the "
-                                           "window's further replays: graph submission and "
-                                           "event cost, paid once per window (so included "
-                                           "in value, spread over its launches)"},
+                   "one_launch_graph_replay_us": round(replay_s * 1e6, 3),
+                   "one_launch_graph_replay_note": "a replay of a graph holding one tiny GEMV "
+                                                   "launch, between events on an idle stream "
+                                                   "(mostly the host's submission latency); "
+                                                   "each timed window starts behind an untimed "
+                                                   "leading replay, so none of it is inside "
+                                                   "the windows"},
         "pct_of_peak": round(100 * value_TBps * 1e12 / PEAK_HBM, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved_GBps, 1), "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": round(achieved_GBps * 1e9 / PEAK_HBM, 4),
