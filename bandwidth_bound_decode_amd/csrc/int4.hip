@@ -308,14 +308,20 @@ __global__ void __launch_bounds__(64 * MAXW)
         const int t = (int)threadIdx.x;
         const int nthreads = (int)blockDim.x;
         const unsigned char *xb = reinterpret_cast<const unsigned char *>(x);
-        constexpr int kMaxCopy = 4;                  // 16-byte copies held per thread
+        // 16-byte copies held per thread: the plans give long rows (K = 14336: 28 KiB of x
+        // over 512 threads) U >= 4 and K = 4096 rows (8 KiB over 256-512 threads) U <= 2;
+        // any x beyond goes through the loop after the burst.
+        constexpr int kMaxCopy = U >= 4 ? 4 : 2;
+        // Unconditional loads from clamped offsets (past the end they re-read the last 16
+        // bytes): loads under a branch, even a workgroup-uniform one, are each waited for
+        // before the join.
         u32x4 cp[kMaxCopy];
 #pragma unroll
         for (int i = 0; i < kMaxCopy; ++i) {
-            const int off = 16 * (t + i * nthreads);
-            if (off < 64 * vecs)
-                cp[i] = *reinterpret_cast<const u32x4 *>(xb + off);
+            const int off = min(16 * (t + i * nthreads), 64 * vecs - 16);
+            cp[i] = *reinterpret_cast<const u32x4 *>(xb + off);
         }
+        __builtin_amdgcn_sched_barrier(0);   // x's loads go out before the weights'
         {
             const uint8_t *wr[R];
             const uint16_t *sr[R];
@@ -350,8 +356,8 @@ __global__ void __launch_bounds__(64 * MAXW)
         const int t = (int)threadIdx.x;
         const int nthreads = (int)blockDim.x;
         unsigned w[16];
-        if (t < vecs) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(x + 32 * t);
+        {   // clamped rather than predicated, for the same reason as the bf16 copy above
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(x + 32 * min(t, vecs - 1));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const u32x4 v = src[j];
@@ -361,6 +367,7 @@ __global__ void __launch_bounds__(64 * MAXW)
                 w[4 * j + 3] = v.w;
             }
         }
+        __builtin_amdgcn_sched_barrier(0);   // x's loads go out before the weights'
         {
             const uint8_t *wr[R];
             const uint16_t *sr[R];

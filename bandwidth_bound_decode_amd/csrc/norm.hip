@@ -116,9 +116,7 @@ __global__ void __launch_bounds__(512) gemv_rmsnorm(NormArgs a)
 
     // u = gamma * h as hi + lo in LDS, and this thread's share of sum h^2.
     float sq = 0.f;
-    for (int v = (int)threadIdx.x; v < vecs; v += (int)blockDim.x) {
-        const u32x4 hv = one ? h0 : load_cached(a.h + kVecElems * v);
-        const u32x4 gv = one ? g0 : load_cached(a.gamma + kVecElems * v);
+    auto stage = [&](int v, u32x4 hv, u32x4 gv) {
         const unsigned hd[4] = {hv.x, hv.y, hv.z, hv.w};
         const unsigned gd[4] = {gv.x, gv.y, gv.z, gv.w};
         unsigned hi[4], lo[4];
@@ -135,6 +133,14 @@ __global__ void __launch_bounds__(512) gemv_rmsnorm(NormArgs a)
         }
         uhi[v] = u32x4{hi[0], hi[1], hi[2], hi[3]};
         ulo[v] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    };
+    // The one-vector case in a block of its own: inside the general loop the compiler waits
+    // for every outstanding load (the weight burst too) before the first vector.
+    if (one) {
+        stage((int)threadIdx.x, h0, g0);
+    } else {
+        for (int v = (int)threadIdx.x; v < vecs; v += (int)blockDim.x)
+            stage(v, load_cached(a.h + kVecElems * v), load_cached(a.gamma + kVecElems * v));
     }
     const float wsq = lane63(wave_sum(sq));
     if (lane == 0)
