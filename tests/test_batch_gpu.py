@@ -77,3 +77,21 @@ def test_batch_unaligned_many_rows(m):
     Y, _ = gemv(W, X)
     oracle_check(W, X, Y, f"unaligned many rows m={m}")
     rows_match_batch_one(W, X, Y)
+
+
+@pytest.mark.parametrize("n,m", [(63, 1), (63, 3), (63, 6), (135, 1), (135, 3), (135, 6),
+                                 (4097, 1), (4097, 3), (4097, 6), (4097, 16)])
+def test_unaligned_tail_rows(n, m):
+    """Rows of a row class past its last whole group of 8 are summed by a whole workgroup
+    with K split over its waves: 63 rows in 8 classes leave one class of 7 rows (all tail
+    rows) beside classes of 8, 135 rows one tail row in seven classes, 4097 one in class 0.
+    Oracle parity and, since which rows are tail rows does not depend on M, every batch row
+    bitwise equal to its batch-1 run; with x staged in chunks at M = 16."""
+    k = 2001 if m < 16 else 9001
+    w, x = draw(n, k, m, seed=500 + n + m)
+    W = device_matrix(w)                 # ldw = k, odd: every row at another 2-byte offset
+    X = device_matrix(x, ld=k + 3, offset=1)
+    Y, p = gemv(W, X)
+    assert p.info["splits"] == 1
+    oracle_check(W, X, Y, f"unaligned tail rows n={n} m={m}")
+    rows_match_batch_one(W, X, Y)
