@@ -1,20 +1,20 @@
-// mfma.hip - skinny-batch GEMV on the matrix cores (by default for 8 <= M <= 16).
+// mfma.hip - skinny-batch GEMV on the matrix cores (by default for 2 <= M <= 16).
 //
 // The VALU kernels multiply every weight vector a lane loads by M input vectors with
-// v_dot2 instructions; past M ~ 8 that arithmetic, not HBM, sets the time (about 0.75 us
-// per extra vector at 4096 x 14336). Here one v_mfma_f32_16x16x32_bf16 takes 16 weight rows
-// (A operand) and 16 input vectors (B operand) over 32 K elements, so the arithmetic per
-// weight byte no longer grows with M. Batches below 16 repeat the last vector in the unused
-// B columns, whose outputs are never stored.
+// v_dot2 instructions, so their time grows with M (about 0.6 us per extra vector at
+// 4096 x 14336: 19.9 us at M = 2, 24.4 at 8, 28.3 at 16). Here one v_mfma_f32_16x16x32_bf16
+// takes 16 weight rows (A operand) and 16 input vectors (B operand) over 32 K elements, so
+// the arithmetic per weight byte does not grow with M (19.3 us at M = 2, 19.8 at 8). Batches
+// below 16 repeat vectors in the unused B columns, whose outputs are never stored.
 //
 // Operand layout of the 16x16x32 bf16 MFMA on gfx950 (checked on the device against an
 // exact integer product): lane l holds A[l % 16][8 (l / 16) .. +8) and B[8 (l / 16) .. +8)
 // [l % 16] as 8 packed bf16, and D[4 (l / 16) + e][l % 16] in accumulator register e. Only
 // the pairing of A and B elements matters to the sum, so K element 32 u + 8 g + e of a chunk
-// goes to lane group g of MFMA u: each 16-byte load then covers 64 contiguous bytes of 16
-// rows (of W) or of 16 vectors (of X).
+// goes to lane group g of MFMA u: every 16-byte operand is 8 contiguous K elements of one
+// row (of W) or one vector (of X).
 //
-// Work split (measured on MI355X at 4096 x 14336, M = 8..16; probe sweeps of tiles per
+// Work split (measured on MI355X at 4096 x 14336, M = 2..16; probe sweeps of tiles per
 // workgroup, chunk sizes, MFMAs per burst, waves per workgroup and split counts):
 //   - a workgroup owns T 16-row tiles and one K slice; its 8 waves take the slice's chunks
 //     in turn, starting at a per-workgroup rotation so that workgroups running side by
