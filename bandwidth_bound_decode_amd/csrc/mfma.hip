@@ -19,10 +19,12 @@
 //   - a workgroup owns T 16-row tiles and one K slice; its 8 waves take the slice's chunks
 //     in turn, starting at a per-workgroup rotation so that workgroups running side by
 //     side read different column ranges of their rows. Two forms: T = 2 with 64-element
-//     chunks for any M up to 16 (the two tiles share every X fragment, halving X traffic
-//     against one tile), and, for M <= 8, T = 1 with 128-element chunks, whose X is only
-//     8 vectors: twice the row blocks, so 4096 rows fill 256 CUs with no split and no
-//     combine (19.8 us against 21.1 us at M = 8);
+//     chunks (the two tiles share every X fragment, halving X traffic against one tile),
+//     and T = 1 with 128-element chunks: twice the row blocks, so 4096 rows fill 256 CUs
+//     with no split and no combine (19.8 us against 21.1 us at M = 8). T = 1 stages 8 X
+//     vectors for M <= 8 and 16 above; with 16 it reads as many X bytes as W bytes at
+//     M = 16, which the split it avoids is worth up to M = 14 at K = 14336 and at every M
+//     at K = 4096 (e.g. 4096 x 4096, M = 9..16: 7.3-7.8 against 9.2 us split);
 //   - a chunk row is one or two 128-byte lines. Loaded straight in the operand layout,
 //     every load instruction touches 16 rows x 64 bytes (half of 16 cache lines); a
 //     read-only probe of that pattern streamed W at 4.3-5.7 TB/s against 6.4 TB/s for
@@ -73,7 +75,8 @@ __device__ __forceinline__ floatx4 mfma(u32x4 a, u32x4 b, floatx4 c)
 // y[m][row] = sum_k w[row][k] x[m][k] for the row block blockIdx.x (T 16-row tiles) and
 // the K slice blockIdx.y (of gridDim.y), in chunks of CH elements. XV: X vectors staged
 // per chunk (16, or 8 when M <= 8: B lanes 8..15 then repeat vectors 0..7, and their
-// output columns are never stored). With one slice the result goes to y; with several,
+// output columns are never stored; vectors past M repeat vector M - 1, whose lines the
+// memory system then fetches once). With one slice the result goes to y; with several,
 // to partial[slice][m][row] and then, by the last arrival, to y.
 template <int T, int XV, int CH>
 __global__ void __launch_bounds__(kThreads)
@@ -253,12 +256,15 @@ gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const
     int n = (int)p->n, k = (int)p->k, ldw = (int)segs[0].ldw, ldxi = (int)ldx,
         ldy = (int)segs[0].ldy, m = p->m, slice = (int)p->mfma_slice;
     void *args[] = {&w, &x, &y, &partial, &tickets, &n, &k, &ldw, &ldxi, &ldy, &m, &slice};
-    const bool narrow = p->mfma_rows == kMfmaNarrowRows;
-    if ((!narrow && p->mfma_rows != kMfmaRowsPerBlock) || (narrow && m > kMfmaNarrowMaxBatch))
+    const void *fn;
+    if (p->mfma_rows == kMfmaRowsPerBlock)
+        fn = reinterpret_cast<const void *>(&gemv_mfma<2, 16, kMfmaChunk>);
+    else if (p->mfma_rows == kMfmaNarrowRows && m <= kMfmaNarrowShortX)
+        fn = reinterpret_cast<const void *>(&gemv_mfma<1, kMfmaNarrowShortX, kMfmaNarrowChunk>);
+    else if (p->mfma_rows == kMfmaNarrowRows)
+        fn = reinterpret_cast<const void *>(&gemv_mfma<1, 16, kMfmaNarrowChunk>);
+    else
         return GEMV_ERR_INVALID_ARG;
-    const void *fn = narrow
-                         ? reinterpret_cast<const void *>(&gemv_mfma<1, 8, kMfmaNarrowChunk>)
-                         : reinterpret_cast<const void *>(&gemv_mfma<2, 16, kMfmaChunk>);
     hipError_t e = hipLaunchKernel(fn,
                                    dim3((unsigned)p->mfma_grid_x, (unsigned)p->mfma_splits),
                                    dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));

@@ -443,13 +443,16 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
         }
     }
 
-    // Matrix-core launch for batches: 16-row workgroups with 128-element chunks for M <= 8
-    // (K a multiple of 128), else 32-row workgroups with 64-element chunks; split over K
-    // (with the same deterministic combine) only while the row blocks alone leave CUs
-    // without one.
+    // Matrix-core launch for batches: 16-row workgroups with 128-element chunks (K a
+    // multiple of 128) for M <= 8, and for larger M while 32-row workgroups would not cover
+    // the CUs and M K stays within kMfmaNarrowMaxMK; else 32-row workgroups with 64-element
+    // chunks. Split over K (with the same deterministic combine) only while the row blocks
+    // alone leave CUs without one.
     int mf = 0, mf_s = 1, mf_depth = 0;
     int64_t mf_slice = k;
-    const bool narrow = m <= kMfmaNarrowMaxBatch && k % kMfmaNarrowChunk == 0;
+    const bool wide_splits = ceil_div(n, (int64_t)kMfmaRowsPerBlock) < dev->compute_units;
+    const bool narrow = k % kMfmaNarrowChunk == 0 &&
+                        (m <= kMfmaNarrowShortX || (wide_splits && (int64_t)m * k <= kMfmaNarrowMaxMK));
     const int mf_rows = narrow ? kMfmaNarrowRows : kMfmaRowsPerBlock;
     const int mf_chunk = narrow ? kMfmaNarrowChunk : kMfmaChunk;
     const int64_t mf_grid = ceil_div(n, mf_rows);

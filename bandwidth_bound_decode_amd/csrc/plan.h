@@ -42,14 +42,23 @@ constexpr int64_t kTicketSlots = 4096;
 // Matrix-core kernel (mfma.hip): workgroups of 8 waves that take K in chunks; used by
 // default from this batch size on (at 4096 x 14336 it is faster than the VALU kernels from
 // M = 2 on: 19.3 against 19.9 us, and 19.8 against 24.4 us at M = 8). Two forms: 32-row
-// blocks with 64-element chunks (any M up to 16), and for M <= 8 16-row blocks with
-// 128-element chunks, whose X is half as many vectors per chunk (measured faster there:
-// twice the row blocks, so 4096 rows fill 256 CUs without a split).
+// blocks with 64-element chunks, whose two 16-row tiles share every X fragment, and 16-row
+// blocks with 128-element chunks, twice the row blocks (4096 rows fill 256 CUs without
+// splitting K). The 16-row form is taken (K a multiple of 128) for M <= 8, where it stages
+// 8 X vectors per chunk, and for M = 9..16 when the 32-row blocks would leave CUs without
+// one (so K would be split) and M K is at most kMfmaNarrowMaxMK: it then reads X twice as
+// often per weight byte but needs no split and no combine. Measured on MI355X, M = 9..16:
+// 4096 x 4096 7.3-7.8 against 9.2 us, 6144 x 4096 11.9-12.7 against 14.7-15.1 us, 1024 x
+// 4096 6.7 against 8.0-8.2 us, 4096 x 14336 20.2-21.6 against 21.5-21.7 us up to M = 14;
+// the forms tie at M = 15 there and the split 32-row form wins at M = 16 (22.1 against
+// 22.3 us). With enough row blocks for the 32-row form (14336 x 4096) it is as fast or
+// faster at every M from 9.
 constexpr int kMfmaRowsPerBlock = 32;
 constexpr int kMfmaChunk = 64;
 constexpr int kMfmaNarrowRows = 16;
 constexpr int kMfmaNarrowChunk = 128;
-constexpr int kMfmaNarrowMaxBatch = 8;
+constexpr int kMfmaNarrowShortX = 8;                    // X vectors staged for M <= 8
+constexpr int64_t kMfmaNarrowMaxMK = 14 * 14336;
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaMinBatch = 2;
 // INT4 weights (int4.hip): 32 weights per 16-byte vector, one bf16 scale per 128.

@@ -805,7 +805,7 @@ def main(argv=None):
                                               "grid_x", "grid_y")}
             if info["mfma"]:      # aligned calls of this plan run the matrix-core kernel
                 r["plan"] = {"kernel": "gemv_mfma", "splits": info["mfma_splits"],
-                             "rows_per_block": 32, "grid_x": info["mfma_grid_x"],
+                             "rows_per_block": info["mfma_rows"], "grid_x": info["mfma_grid_x"],
                              "grid_y": info["mfma_splits"]}
             for k in list(r):
                 if isinstance(r[k], float):

@@ -73,7 +73,7 @@ typedef struct gemv_plan_s *gemv_plan_t;
  *                   vectors the work stops being a matrix-vector product and matrix units
  *                   start to pay; on MI355X they do from M = 2): 0 = automatic (M >= 2
  *                   with no tile, split or cap forced), 1 = for any M >= 2, -1 = never. It
- *                   needs K to be a multiple of 64 (of 128 for the 16-row form, M <= 8).
+ *                   needs K to be a multiple of 64 (of 128 for the 16-row form).
  *                   It runs only for 16-byte-aligned single-matrix calls; other calls of
  *                   the same plan take the VALU kernels the fields above describe. The
  *                   VALU kernels sum every output in the same order at every M, so with
@@ -139,9 +139,10 @@ typedef struct {
     int weights;            /* the plan's weight format */
     int prologue;           /* the plan's input prologue (0: none) */
     int int4_fp16;          /* INT4: 1 when the workgroups try the fp16 form of staged x */
-    int mfma_rows;          /* rows per matrix-core workgroup: 16 (M <= 8 and K a multiple
-                               of 128; chunks of 128 K elements) or 32 (chunks of 64); 0
-                               without the matrix-core launch */
+    int mfma_rows;          /* rows per matrix-core workgroup: 16 (K a multiple of 128, and
+                               M <= 8 or, for M = 9..16, 32-row blocks too few for the
+                               CUs with M K <= 14 * 14336; chunks of 128 K elements) or 32
+                               (chunks of 64); 0 without the matrix-core launch */
 } gemv_plan_info;
 
 /*

@@ -1,6 +1,7 @@
-"""GPU parity of the matrix-core batch kernel (both forms: 16-row blocks for M <= 8, 32-row
-blocks otherwise): within tolerance of the oracle at the down_proj shape and on small shapes
-that span several row blocks with a ragged last one,
+"""GPU parity of the matrix-core batch kernel (its three instances: 16-row blocks staging 8 X
+vectors for M <= 8, 16-row blocks staging 16 for larger M where 32-row blocks would split K,
+32-row blocks otherwise): within tolerance of the oracle at the down_proj shape and on small
+shapes that span several row blocks with a ragged last one,
 unsplit and split over K; exact where every partial sum is exact (identity, one-hot, constant
 W); reproducible bit for bit; and the unaligned fallback equal to the VALU plan."""
 import numpy as np
@@ -15,12 +16,12 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("m", [8, 12, 16])
 def test_down_proj_batches(m):
-    """Full size: M = 8 on the 16-row form (unsplit), M = 12 and 16 on the 32-row form (two
-    slices and the combine)."""
+    """Full size: M = 8 and 12 on the 16-row form (unsplit; 8 and 16 X vectors), M = 16 on
+    the 32-row form (two slices and the combine)."""
     w, x = draw(4096, 14336, m, seed=300 + m)
     W, X = device_matrix(w), device_matrix(x)
     Y, p = gemv(W, X)
-    want = (16, 1) if m <= 8 else (32, 2)
+    want = (16, 1) if m <= 14 else (32, 2)
     assert p.info["mfma"] == 1 and (p.info["mfma_rows"], p.info["mfma_splits"]) == want, p.info
     oracle_check(W, X, Y, f"mfma down m={m}")
     Y2, _ = gemv(W, X, plan=p)
@@ -41,25 +42,30 @@ def test_shapes_every_batch(n, k):
         assert bits_equal(Y, Y2), f"n={n} k={k} m={m} not reproducible"
 
 
-@pytest.mark.parametrize("m", [16, 8])
-def test_identity_and_one_hot_exact(m):
-    n = k = 512
+@pytest.mark.parametrize("m,rows", [(16, 32), (16, 16), (8, 16)])
+def test_identity_and_one_hot_exact(m, rows):
+    """Every form: K a multiple of 128 takes the 16-row form at these sizes, K = 576 and 4160
+    (64 past a multiple of 128) the 32-row one. One-hot columns sit at the ends of K, on
+    MFMA, piece and line edges of a chunk and on slice boundaries."""
+    n = k = 512 if rows == 16 else 576
     _, x = draw(1, k, m, seed=7)
     eye = torch.eye(n, dtype=torch.bfloat16)
     Y, p = gemv(device_matrix(eye), device_matrix(x), mfma=1)
-    assert p.info["mfma"] == 1 and p.info["mfma_rows"] == (16 if m <= 8 else 32)
+    assert p.info["mfma"] == 1 and p.info["mfma_rows"] == rows
     assert bits_equal(Y, x.float()), "W = I must return X exactly"
-    w, _ = draw(300, 4096, 1, seed=8)
-    cols = [0, 1, 31, 32, 63, 64, 511, 512, 2047, 2048, 4032, 4095, 7, 100, 3000, 4094]
-    if m <= 8:   # both lines, every MFMA and piece of a 128-element chunk, and slice edges
-        cols = [0, 33, 71, 127, 128, 1023, 2050, 4095]
-    xo = torch.zeros(m, 4096, dtype=torch.bfloat16)
-    for i, c in enumerate(cols):
-        xo[i, c] = 1.0
+    kw = 4096 if rows == 16 else 4160
+    w, _ = draw(300, kw, 1, seed=8)
+    if rows == 32:       # 64-element chunks, slices of 576
+        cols = [0, 1, 31, 32, 63, 64, 575, 576, 2047, 2048, 4032, 4159, 7, 100, 3000, 4158]
+    else:                # 128-element chunks, slices of 1024 (both lines, every MFMA and piece)
+        cols = [0, 33, 71, 127, 128, 1023, 2050, 4095, 1, 32, 64, 96, 1024, 3968, 2048, 2047]
+    xo = torch.zeros(m, kw, dtype=torch.bfloat16)
+    for i in range(m):
+        xo[i, cols[i]] = 1.0
     Y, p = gemv(device_matrix(w), device_matrix(xo), mfma=1)
-    assert p.info["mfma_splits"] > 1
-    for i, c in enumerate(cols):
-        assert bits_equal(Y[i], w[:, c].float()), f"one-hot column {c}"
+    assert p.info["mfma_rows"] == rows and p.info["mfma_splits"] > 1, p.info
+    for i in range(m):
+        assert bits_equal(Y[i], w[:, cols[i]].float()), f"one-hot column {cols[i]}"
 
 
 def test_constant_w_exact():
@@ -89,23 +95,26 @@ def test_accumulator_rounded_once_per_mfma():
     assert bits_equal(Y, torch.full((m, n), 1.0 + 2.0 ** -20)), Y[0, :4].tolist()
 
 
-@pytest.mark.parametrize("m", [9, 8])
-def test_special_values(m):
-    n, k = 64, 1024
+@pytest.mark.parametrize("m,k,rows", [(9, 1024, 16), (8, 1024, 16), (16, 1088, 32)])
+def test_special_values(m, k, rows):
+    n = 64
     w, x = draw(n, k, m, seed=10)
     w[3, 17] = float("inf")
     w[5, 900] = float("nan")
     x[:, 17] = 1.0
-    Y, _ = gemv(device_matrix(w), device_matrix(x), mfma=1)
+    Y, p = gemv(device_matrix(w), device_matrix(x), mfma=1)
+    assert p.info["mfma_rows"] == rows, p.info
     assert torch.isinf(Y[:, 3]).all() and torch.isnan(Y[:, 5]).all()
     keep = [i for i in range(n) if i not in (3, 5)]
     assert torch.isfinite(Y[:, keep]).all()
 
 
-def test_accumulator_rounded_once_per_mfma_narrow():
-    """The same pin on the 16-row form: K = 128 is one chunk, four MFMAs in order on one
-    wave; the first gives exactly 1.0 and each later one adds 32 products of 2^-25."""
-    n, k, m = 16, 128, 8
+@pytest.mark.parametrize("m", [8, 16])
+def test_accumulator_rounded_once_per_mfma_narrow(m):
+    """The same pin on the 16-row form (8 and 16 X vectors): K = 128 is one chunk, four MFMAs
+    in order on one wave; the first gives exactly 1.0 and each later one adds 32 products of
+    2^-25."""
+    n, k = 16, 128
     w = torch.zeros(n, k, dtype=torch.bfloat16)
     w[:, 0] = 1.0
     w[:, 32:] = 2.0 ** -25

@@ -78,8 +78,11 @@ def test_mi355x_plans(n, k, m):
         assert p.workspace_size == 0
     if info["mfma"]:
         ms, msl, rows = info["mfma_splits"], info["mfma_slice"], info["mfma_rows"]
-        # 16-row blocks with 128-element chunks for M <= 8, else 32-row with 64-element ones
-        assert rows == (16 if m <= 8 and k % 128 == 0 else 32)
+        # 16-row blocks with 128-element chunks for M <= 8, and above while 32-row blocks
+        # would not cover the 256 CUs and M K <= 14 * 14336; else 32-row with 64-element ones
+        wide_splits = math.ceil(n / 32) < 256
+        assert rows == (16 if k % 128 == 0 and (m <= 8 or wide_splits and m * k <= 14 * 14336)
+                        else 32)
         chunk = 128 if rows == 16 else 64
         assert m >= 2 and k % chunk == 0 and msl % chunk == 0
         assert (ms - 1) * msl < k <= ms * msl
@@ -238,7 +241,15 @@ def test_mfma_plans():
     assert e["mfma_depth_bound"] == 32 + 4 * 14 + 7
     assert plan(4096, 14336, 8).workspace_size == 0
     assert plan(4096, 4160, 8).info["mfma_rows"] == 32     # K not a multiple of 128
-    assert plan(4096, 14336, 9).info["mfma_rows"] == 32
+    # M = 9..14 at 4096 rows: the 16-row form (16 X vectors) instead of splitting K
+    n9 = plan(4096, 14336, 9).info
+    assert (n9["mfma_rows"], n9["mfma_splits"], n9["mfma_grid_x"]) == (16, 1, 256)
+    assert plan(4096, 14336, 14).info["mfma_rows"] == 16
+    assert plan(4096, 14336, 15).info["mfma_rows"] == 32      # M K past 14 * 14336
+    assert plan(4096, 4096, 16).info["mfma_rows"] == 16
+    assert plan(4096, 4096, 16).workspace_size == 0
+    assert plan(8192, 4096, 12).info["mfma_rows"] == 32       # 256 row blocks of 32
+    assert plan(8160, 4096, 12).info["mfma_rows"] == 16       # 255
     assert plan(4096, 14336, 2).info["mfma"] == 1           # the default from M = 2
     assert plan(4096, 14336, 2).info["mfma_rows"] == 16
     assert plan(4096, 14336, 16, mfma=-1).info["mfma"] == 0
@@ -253,8 +264,9 @@ def test_mfma_plans():
     g = plan(28672, 4096, 16).info                            # 896 blocks: no split
     assert (g["mfma"], g["mfma_splits"]) == (1, 1)
     assert plan(28672, 4096, 16).workspace_size == 0
-    small = plan(33, 4096, 9).info                            # 2 blocks: split to the cap
-    assert small["mfma_splits"] == 4096 // 512 and small["mfma_slice"] == 512
+    small = plan(33, 4160, 9).info                            # 2 blocks: split to the cap
+    assert small["mfma_rows"] == 32
+    assert small["mfma_splits"] == 8 and small["mfma_slice"] == 576
     small8 = plan(33, 4096, 8).info                           # 3 narrow blocks: the same
     assert small8["mfma_rows"] == 16 and small8["mfma_grid_x"] == 3
     assert small8["mfma_splits"] == 4096 // 1024 and small8["mfma_slice"] == 1024
