@@ -150,7 +150,7 @@ struct gemv_plan_s {
     int64_t mfma_slice;
     int mfma_grid_x;
     int mfma_depth;
-    int mfma_rows;              // rows per matrix-core workgroup: 32, or 16 (M <= 8)
+    int mfma_rows;              // rows per matrix-core workgroup: 32 or 16
     int weights;                // GEMV_WEIGHTS_BF16 or GEMV_WEIGHTS_INT4
     int prologue;               // 0 or GEMV_PROLOGUE_RMSNORM
     int int4_fp16;              // INT4 with x in LDS: the workgroups try the fp16 staging
