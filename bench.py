@@ -803,7 +803,11 @@ def main(argv=None):
             info = r["plan"]
             r["plan"] = {k: info[k] for k in ("splits", "rows_per_wave", "unroll",
                                               "grid_x", "grid_y")}
-            if info["mfma"]:      # aligned calls of this plan run the matrix-core kernel
+            if gg.k % 8 and not segs and info["splits"] == 1:
+                # contiguous rows of odd length sit at 2-byte offsets: the call takes the
+                # class-staged unaligned kernel, whose wave shape is its own (not the plan's)
+                r["plan"] = {"kernel": "gemv_unaligned_lds", "splits": 1}
+            elif info["mfma"]:    # aligned calls of this plan run the matrix-core kernel
                 r["plan"] = {"kernel": "gemv_mfma", "splits": info["mfma_splits"],
                              "rows_per_block": info["mfma_rows"], "grid_x": info["mfma_grid_x"],
                              "grid_y": info["mfma_splits"]}
