@@ -790,6 +790,12 @@ def main(argv=None):
                        ()))
         for gg, (ww, xx) in zip(workloads.SKINNY_BATCH.gemvs, workloads.draw_config(workloads.SKINNY_BATCH)):
             shapes.append((gg.name, gg, ww, xx, ()))
+        # batches of 9-16 on the 16-row matrix-core form with 16 X vectors (where 32-row blocks
+        # would have to split K): down_proj at M = 12 and o_proj at M = 16
+        for name, n, k, m in (("batch_m12", workloads.HIDDEN, workloads.INTERMEDIATE, 12),
+                              ("o_proj_m16", 4096, 4096, 16)):
+            gb = workloads.Gemv(name, n, k, m)
+            shapes.append((name, gb, *workloads.draw_gemv(gb, workloads.generator(70 + m)), ()))
         # the unaligned 4097 x 14337 tail at the batches where x no longer fits in LDS whole
         for m in (8, 16):
             gt = workloads.Gemv(f"skinny_tail_m{m}", workloads.HIDDEN + 1,
