@@ -304,18 +304,21 @@ gemv_status plan_rmsnorm(gemv_plan_t *out, int64_t n, int64_t k, int m,
     p->waves_per_block = waves;
     p->unroll = u;
     p->slice = k;
-    // Workgroups loop over row blocks, so the staging is paid once per workgroup rather than
-    // once per block: the grid holds two workgroups per CU, four when there are more than
-    // four blocks per CU (measured: QKV 9.6 us at two against 11.0 us with one workgroup per
-    // block; gate_up 35.1 us at four against 36.2 at two), or as many as opts.waves_per_cu
-    // allows (-1: one workgroup per block, no loop).
+    // Up to four row blocks per CU the workgroups loop over row blocks, two per CU, so the
+    // staging is paid once per workgroup rather than once per block (measured: QKV 9.3 us
+    // against 10.1 us with one workgroup per block). Beyond that every block gets a workgroup
+    // of its own and the dispatcher hands them to whichever CU frees up, where looping
+    // workgroups would each own a fixed share (gate_up 35.5-36.0 against 36.1-36.8 us with
+    // four looping workgroups per CU, lm_head 149-152 against 163 us). opts.waves_per_cu
+    // sets the looping grid's workgroups per CU instead, -1 one workgroup per block.
     const int64_t blocks = ceil_div(n, waves);
-    int64_t per_cu_blocks = blocks > (int64_t)kNormManyBlocksPerCU * dev->compute_units
-                                ? kNormManyBlocksPerCU
-                                : kNormBlocksPerCU;
+    const bool many = blocks > (int64_t)kNormManyBlocksPerCU * dev->compute_units;
+    int64_t per_cu_blocks = kNormBlocksPerCU;
     if (o.waves_per_cu > 0)
         per_cu_blocks = o.waves_per_cu >= waves ? o.waves_per_cu / waves : 1;
-    const int64_t most = o.waves_per_cu < 0 ? blocks : per_cu_blocks * dev->compute_units;
+    const int64_t most = o.waves_per_cu < 0 || (many && o.waves_per_cu == 0)
+                             ? blocks
+                             : per_cu_blocks * dev->compute_units;
     p->grid_x = (int)(blocks < most ? blocks : most);
     p->grid_y = 1;
     p->block_threads = kWaveLanes * waves;

@@ -115,7 +115,7 @@ gemv_status launch_rmsnorm(gemv_plan_t p, const gemv_segment *segs, int nseg, co
                            const void *gamma, float eps, void *stream);
 constexpr int64_t kNormMaxK = 16368;   // 4K + 64 bytes of LDS (hi and lo halves, wave sums)
 constexpr int kNormBlocksPerCU = 2;       // RMSNorm-prologue workgroups per CU in the grid,
-constexpr int kNormManyBlocksPerCU = 4;   // or this many beyond as many row blocks per CU
+constexpr int kNormManyBlocksPerCU = 4;   // or one per row block beyond this many blocks per CU
 
 // INT4-weight launch (int4.hip) of a validated call; the plan's unroll, rows per wave and
 // LDS size pick the kernel.

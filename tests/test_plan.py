@@ -337,7 +337,9 @@ def test_rmsnorm_plans():
     assert (i["rows_per_wave"], i["waves_per_block"], i["unroll"]) == (1, 8, 8)
     assert (i["grid_x"], i["block_threads"], i["lds_bytes"]) == (512, 512, 32 * 512 + 4 * 8)
     assert plan(1024, 4096, prologue="rmsnorm").info["grid_x"] == 128   # one row block each
-    assert plan(28672, 4096, prologue="rmsnorm").info["grid_x"] == 1024  # 14 blocks per CU
+    assert plan(28672, 4096, prologue="rmsnorm").info["grid_x"] == 3584  # 14 blocks per CU:
+    assert plan(8200, 4096, prologue="rmsnorm").info["grid_x"] == 1025   # one workgroup each
+    assert plan(8192, 4096, prologue="rmsnorm").info["grid_x"] == 512    # 4 per CU: looping
     # 4 dot2 per vector x 8 vectors + 8, half of (4 + 1 + 6 + 7) rounded up, 4 for the scale
     assert i["depth_bound"] == 40 + 9 + 4
     assert plan(6144, 4096, prologue="rmsnorm").workspace_size == 0

@@ -50,6 +50,13 @@ def test_llama_projections(segments):
     Y, p = run(parts, h, gain)
     print(segments, p.info, flush=True)
     check(w, h, gain, Y, f"rmsnorm {segments}")
+    # The other grid form (looping workgroups, or one workgroup per row block) sums every row
+    # in the same order, so it gives the same bits.
+    blocks = -(-sum(segments) // 8)
+    other = dict(waves_per_cu=-1) if p.info["grid_x"] < blocks else dict(waves_per_cu=8)
+    Y2, p2 = run(parts, h, gain, **other)
+    assert p2.info["grid_x"] != p.info["grid_x"]
+    assert bits_equal(Y, Y2), f"grid {p2.info['grid_x']} differs from grid {p.info['grid_x']}"
 
 
 @pytest.mark.parametrize("n,k", [(7, 8), (33, 1000), (129, 4104), (300, 2048), (17, 8192)])
