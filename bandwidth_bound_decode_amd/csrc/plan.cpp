@@ -45,7 +45,9 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // four-row waves at every Llama-8B shape once the resident-wave cap below is applied).
 //   - Rows of more than 8 wave steps (K > 4096) are read in bursts of 4 steps.
 //   - Shorter rows are read in one burst when the grid needs more than one round of
-//     waves, and in bursts of up to 4 steps when it fits in one round.
+//     waves, and in bursts of up to 4 steps when it fits in one round; beyond one round
+//     (and for single-step rows from kShortRowBlockMinRows rows) kShortRowWaves of them
+//     share a workgroup.
 // Larger M spends VGPRs on X vectors and accumulators, so the W unroll shrinks. Every
 // choice gives bitwise the same result.
 void default_tile(int m, int64_t n, int64_t k, int cus, int *r, int *u, int *waves)
@@ -53,7 +55,10 @@ void default_tile(int m, int64_t n, int64_t k, int cus, int *r, int *u, int *wav
     int64_t steps = (k + kWaveStep - 1) / kWaveStep;
     if (m == 1) {
         *r = 1;
-        *waves = 1;
+        const bool many = n > (int64_t)kOneRoundWavesPerCU * cus;
+        *waves = steps < 8 && (many || (steps == 1 && n >= kShortRowBlockMinRows))
+                     ? kShortRowWaves
+                     : 1;
         if (steps > 8)
             *u = 4;
         else if (steps <= 2)
@@ -81,14 +86,14 @@ void default_tile(int m, int64_t n, int64_t k, int cus, int *r, int *u, int *wav
 }
 
 // Automatic resident-wave cap per CU (0: none) for a batch-1 unsplit launch of `waves_total`
-// single-wave workgroups. Measured on MI355X (down_proj 4096 x 14336: 18.36 us capped at 8
+// single-wave workgroups (multi-wave workgroups measured faster uncapped). Measured on MI355X (down_proj 4096 x 14336: 18.36 us capped at 8
 // in two equal rounds, 18.97 us uncapped in one round of 16, 20.1 us at 12 in unequal
 // rounds; gate_up, QKV and the LM head: best near 12). A cap makes the workgroups of later
 // rounds start wherever a CU frees up, which evens out the finish times of the CUs; the cap
 // is spread so that all rounds are equally full.
-int auto_cap(int m, int s, int64_t k, int64_t waves_total, int cus)
+int auto_cap(int m, int s, int waves, int64_t k, int64_t waves_total, int cus)
 {
-    if (m != 1 || s != 1)
+    if (m != 1 || s != 1 || waves != 1)
         return 0;
     const int64_t steps = (k + kWaveStep - 1) / kWaveStep;
     const int64_t per_cu = ceil_div(waves_total, cus);
@@ -434,7 +439,7 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
         const int64_t total = ceil_div(n, (int64_t)r * waves) * s * waves;
         const int cap = o.waves_per_cu > 0   ? o.waves_per_cu
                         : o.waves_per_cu < 0 ? 0
-                                             : auto_cap(m, s, k, total, dev->compute_units);
+                                             : auto_cap(m, s, waves, k, total, dev->compute_units);
         if (cap > 0) {
             cap_blocks = cap / waves;
             cap_lds = lds_for_blocks(cap_blocks, kLdsGranule);

@@ -34,6 +34,16 @@ constexpr double kDefaultLatency = 0.65e-6;
 constexpr int kCapLongRows = 8;
 constexpr int kCapShortRows = 12;
 constexpr int kOneRoundWavesPerCU = 16;   // short rows: up to this many waves per CU run
+// Batch-1 rows shorter than 8 wave steps (K < 4096) run in uncapped workgroups of
+// kShortRowWaves waves when the rows need more than one round of kOneRoundWavesPerCU
+// single-wave workgroups per CU, or are a single wave step long (K <= 512) and number at
+// least kShortRowBlockMinRows: single-wave workgroups that stream a few KiB each are then
+// handed out slower than they finish (measured on MI355X: 8192 x 1024 5.98 -> 4.46 us,
+// 16384 x 2048 13.8 -> 11.3 us, 4096 x 512 2.93 -> 2.54 us, 2048 x 512 2.44 -> 2.27 us;
+// within one round at 2-7 steps, 4096 x 1024..3584, between -4 % and +3 %, so those keep
+// single-wave workgroups, as do 1024 rows and K = 4096).
+constexpr int64_t kShortRowBlockMinRows = 2048;
+constexpr int kShortRowWaves = 8;
                                           // as one round, uncapped
 // Ticket counters sit at the start of a split plan's workspace in a region of at least this
 // many slots, so that plans with up to this many row blocks can share one workspace in any

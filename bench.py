@@ -493,6 +493,50 @@ def bench_decode_step(torch, bbd, workloads, replays, warmup):
     return out
 
 
+def bench_shards(torch, bbd, workloads, steps, replays):
+    """One GPU's share of a decode step spread over G GPUs (G = 2, 4, 8): each projection's
+    shard (rows of QKV, gate_up and lm_head, K of o_proj and down_proj) timed back to back on
+    rotated weights like the shapes above, and the per-GPU 129-GEMV sequence as one graph.
+    The collectives a multi-GPU step adds (the K-sharded partials summed over the GPUs, any
+    gather of y) are not built, so the step is the GEMV part of one GPU's time."""
+    from bandwidth_bound_decode_amd.decode_step import Call, Sequence
+    out = []
+    for gpus in workloads.SHARD_GPUS:
+        rec = {"gpus": gpus, "shapes": []}
+        for i, g in enumerate(workloads.shard_gemvs(gpus)):
+            w, x = workloads.draw_gemv(g, workloads.generator(6000 + 10 * gpus + i, "cuda"),
+                                       "cuda")
+            r, _, _, _ = bench_gemv(torch, bbd, g, w, x, steps, 10, g.segments, windows=5)
+            info = r["plan"]
+            rec["shapes"].append({
+                "name": g.name, "shape": f"{g.n}x{g.k}", "alg_bytes": g.alg_bytes,
+                "us_per_launch": round(r["us_per_launch"], 3), "TBps": round(r["TBps"], 4),
+                "pct_peak": round(r["pct_peak"], 2),
+                "plan": {k: info[k] for k in ("splits", "unroll", "grid_x", "waves_per_cu")}})
+            del w, x
+        drawn = workloads.draw_decode_step("cuda", seed=6100 + gpus,
+                                           gemvs=workloads.shard_decode_step_gemvs(gpus))
+        calls = [Call(parts, x, [torch.empty((x.shape[0], w.shape[0]), device="cuda")
+                                 for w in parts]) for _, parts, x in drawn]
+        seq = Sequence(calls)
+        nb = seq.alg_bytes
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            seq.capture(stream)
+            _, per = time_launches(torch, lambda i: seq.replay(stream), replays, 3, stream)
+        t = statistics.median(per)
+        rec["decode_step"] = {"gemvs": len(calls), "alg_bytes": nb,
+                              "graph_ms_median": round(t * 1e3, 4),
+                              "graph_TBps": round(nb / t / 1e12, 4),
+                              "graph_mbu": round(mbu(nb, t, PEAK_HBM), 4),
+                              "at_peak_ms": round(nb / PEAK_HBM * 1e3, 4)}
+        seq.graph.destroy()
+        del seq, calls, drawn
+        torch.cuda.empty_cache()
+        out.append(rec)
+    return out
+
+
 def cpu_baseline(w, x, runs=3):
     """The oracle as it stands, on all host threads, over the same full GEMV."""
     import oracle
@@ -648,17 +692,17 @@ def main(argv=None):
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--sections", default="all",
                     help="comma list of what to run besides the headline: calib, shapes, "
-                         "rmsnorm, int4, decode, decode_int4, cpu (default: all)")
+                         "rmsnorm, int4, decode, decode_int4, shards, cpu (default: all)")
     args = ap.parse_args(argv)
     args.windows = max(5, args.windows)
-    every = {"calib", "shapes", "rmsnorm", "int4", "decode", "decode_int4", "cpu"}
+    every = {"calib", "shapes", "rmsnorm", "int4", "decode", "decode_int4", "shards", "cpu"}
     wanted = every if args.sections == "all" else set(args.sections.split(","))
     if wanted - every:
         ap.error(f"unknown sections {sorted(wanted - every)}")
     if args.skip_shapes:
         wanted -= {"shapes", "rmsnorm", "int4"}
     if args.skip_decode:
-        wanted -= {"decode", "decode_int4"}
+        wanted -= {"decode", "decode_int4", "shards"}
     if args.skip_cpu:
         wanted -= {"cpu"}
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -859,6 +903,15 @@ def main(argv=None):
             f"{d['eager_ms_median']:.3f} ms; graph with {d['rmsnorm_prologue_calls']} fused "
             f"RMSNorm prologues {d['graph_with_rmsnorm_prologues_ms_median']:.3f} ms")
         torch.cuda.empty_cache()
+    if "shards" in wanted:
+        out["shards"] = bench_shards(torch, bbd, workloads, args.shape_steps,
+                                     args.decode_replays)
+        for rec in out["shards"]:
+            d = rec["decode_step"]
+            log(f"one GPU of {rec['gpus']}: " + ", ".join(
+                f"{s['name']} {s['us_per_launch']:.2f} us ({s['pct_peak']:.0f} %)"
+                for s in rec["shapes"]) + f"; per-GPU step {d['graph_ms_median']:.3f} ms "
+                f"(MBU {d['graph_mbu']:.3f}, {d['at_peak_ms']:.3f} ms at peak)")
     if "decode_int4" in wanted:
         d4 = bench_decode_step_int4(torch, bbd, workloads, args.decode_replays)
         for k in list(d4):

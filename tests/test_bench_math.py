@@ -7,6 +7,7 @@ import sys
 import pytest
 
 import bench
+import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_worked_numbers.json")))
@@ -65,3 +66,25 @@ def test_more_than_one_gpu_is_refused():
     assert proc.returncode == 2
     assert "one GPU" in proc.stderr
     assert proc.stdout == ""
+
+
+def test_shard_shapes_cover_the_step():
+    """One GPU's shares times G give back every projection: rows for QKV, gate_up and
+    lm_head (every fused segment cut alike), K for o_proj and down_proj; the per-GPU step's
+    weight bytes are the full step's divided by G."""
+    full = {g.name: g for g in workloads.decode_step_gemvs(1)}
+    lm = workloads.decode_step_gemvs(1)[-1]
+    for gpus in workloads.SHARD_GPUS:
+        qkv, o, gu, down, lm_s = workloads.shard_gemvs(gpus)
+        assert (qkv.n * gpus, qkv.k) == (full["L0.qkv"].n, full["L0.qkv"].k)
+        assert tuple(s * gpus for s in qkv.segments) == full["L0.qkv"].segments
+        assert tuple(s * gpus for s in gu.segments) == full["L0.gate_up"].segments
+        assert (o.n, o.k * gpus) == (full["L0.o"].n, full["L0.o"].k)
+        assert (down.n, down.k * gpus) == (full["L0.down"].n, full["L0.down"].k)
+        assert (lm_s.n * gpus, lm_s.k) == (lm.n, lm.k)
+        step = workloads.shard_decode_step_gemvs(gpus)
+        whole = workloads.decode_step_gemvs()
+        assert len(step) == len(whole) == 129
+        assert sum(2 * g.n * g.k for g in step) * gpus == sum(2 * g.n * g.k for g in whole)
+    with pytest.raises(ValueError):
+        workloads.shard_gemvs(3)

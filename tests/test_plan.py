@@ -177,6 +177,30 @@ def test_batch1_tiles_and_caps(nk):
         assert i["lds_bytes"] == 0
 
 
+# batch-1 rows shorter than 8 wave steps: 8 waves per uncapped workgroup beyond one round of
+# 16 single-wave workgroups per CU, or for single-step rows from 2048 rows
+SHORT_ROWS = {(4096, 512): 2, (2048, 512): 2, (8192, 1024): 2, (4097, 1792): 4,
+              (16384, 2048): 4, (6144, 3584): 8}
+
+
+@pytest.mark.parametrize("nk", sorted(SHORT_ROWS))
+def test_short_rows_share_workgroups(nk):
+    i = plan(*nk).info
+    assert (i["rows_per_wave"], i["unroll"], i["waves_per_block"]) == (1, SHORT_ROWS[nk], 8)
+    assert i["waves_per_cu"] == 0 and i["lds_bytes"] == 0 and i["splits"] == 1
+    assert i["grid_x"] == math.ceil(nk[0] / 8)
+    # rows of 8 wave steps and more keep single-wave workgroups
+    assert plan(nk[0], 4096).info["waves_per_block"] == 1
+    # a forced multi-wave workgroup gets no automatic cap either
+    assert plan(28672, 4096, waves_per_block=4).info["waves_per_cu"] == 0
+
+
+@pytest.mark.parametrize("nk", [(4096, 1024), (4096, 1792), (4096, 3584), (2047, 512),
+                                (1024, 1024), (1024, 4096)])
+def test_short_rows_within_one_round_stay_single_wave(nk):
+    assert plan(*nk).info["waves_per_block"] == 1
+
+
 def test_cap_only_for_unsplit_batch1():
     assert plan(4096, 14336, 2).info["waves_per_cu"] == 0
     assert plan(4096, 14336, splits=2).info["waves_per_cu"] == 0

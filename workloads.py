@@ -82,6 +82,35 @@ SKINNY_BATCH = Config(
     tuple(Gemv(f"skinny_m{m}", HIDDEN, INTERMEDIATE, m) for m in (1, 2, 4, 8, 16))
     + (Gemv("skinny_tail_m3", HIDDEN + 1, INTERMEDIATE + 1, 3),))
 
+# One GPU's share of each projection when a decode step is spread over `gpus` GPUs: the
+# row-independent projections (QKV, gate_up, lm_head) by rows, every segment of a fused one
+# cut alike; o_proj and down_proj by K (each GPU then holds a partial y that a sum over the
+# GPUs completes). Every dimension divides evenly for gpus in {1, 2, 4, 8}.
+SHARD_GPUS = (2, 4, 8)
+
+
+def shard_gemvs(gpus: int) -> tuple[Gemv, ...]:
+    """The five projection shapes of one layer (and lm_head) on one of `gpus` GPUs."""
+    if gpus < 1 or any(d % gpus for d in (Q_ROWS, KV_ROWS, HIDDEN, INTERMEDIATE, VOCAB)):
+        raise ValueError(f"the Llama shapes do not split evenly over {gpus} GPUs")
+    q, kv, i = Q_ROWS // gpus, KV_ROWS // gpus, INTERMEDIATE // gpus
+    return (Gemv(f"qkv_g{gpus}", q + 2 * kv, HIDDEN, segments=(q, kv, kv)),
+            Gemv(f"o_proj_g{gpus}", HIDDEN, HIDDEN // gpus),
+            Gemv(f"gate_up_g{gpus}", 2 * i, HIDDEN, segments=(i, i)),
+            Gemv(f"down_g{gpus}", HIDDEN, INTERMEDIATE // gpus),
+            Gemv(f"lm_head_g{gpus}", VOCAB // gpus, HIDDEN))
+
+
+def shard_decode_step_gemvs(gpus: int, layers: int = LAYERS) -> tuple[Gemv, ...]:
+    """One GPU's GEMV sequence of a decode step spread over `gpus` GPUs, in stream order."""
+    qkv, o, gu, down, lm = shard_gemvs(gpus)
+    seq = []
+    for layer in range(layers):
+        seq += [Gemv(f"L{layer}.{g.name}", g.n, g.k, segments=g.segments) for g in (qkv, o, gu, down)]
+    seq.append(lm)
+    return tuple(seq)
+
+
 # Every workload above, smallest first.
 WORKLOADS: tuple[Config, ...] = (K_PROJ_AND_TAILS, DOWN_PROJ, FUSED_PROJECTIONS, DECODE_STEP,
                                  SKINNY_BATCH)
@@ -120,16 +149,16 @@ def bf16_bits(t: torch.Tensor):
 
 
 def draw_decode_step(device: str | torch.device = "cuda", layers: int = LAYERS,
-                     seed: int | None = None):
+                     seed: int | None = None, gemvs: tuple[Gemv, ...] | None = None):
     """Draw the decode-step sequence: for each GEMV in stream order, its weight (as separate
     contiguous tensors, one per segment of a fused projection) and its input vector.
 
     Returns a list of (Gemv, [W parts], X). About 15 GB of weights at 32 layers, so draw on
-    the GPU.
+    the GPU. `gemvs` replaces the sequence (e.g. one GPU's shard of it).
     """
     gen = generator(DECODE_STEP.seed if seed is None else seed, device)
     out = []
-    for g in decode_step_gemvs(layers):
+    for g in gemvs if gemvs is not None else decode_step_gemvs(layers):
         w, x = draw_gemv(g, gen, device)
         if g.segments:
             parts = [t.clone() for t in torch.split(w, list(g.segments), 0)]
