@@ -45,9 +45,10 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // four-row waves at every Llama-8B shape once the resident-wave cap below is applied).
 //   - Rows of more than 8 wave steps (K > 4096) are read in bursts of 4 steps.
 //   - Shorter rows are read in one burst when the grid needs more than one round of
-//     waves, and in bursts of up to 4 steps when it fits in one round; beyond one round
-//     (and for single-step rows from kShortRowBlockMinRows rows) kShortRowWaves of them
-//     share a workgroup.
+//     waves (of up to 4 steps when rows are that short); when it fits in one round, in
+//     the shortest burst (2, 4 or 8 steps, at most the row) that keeps kBurstTargetBytes
+//     in flight per CU. Beyond one round (and for single-step rows from
+//     kShortRowBlockMinRows rows) kShortRowWaves of them share a workgroup.
 // Larger M spends VGPRs on X vectors and accumulators, so the W unroll shrinks. Every
 // choice gives bitwise the same result.
 void default_tile(int m, int64_t n, int64_t k, int cus, int *r, int *u, int *waves)
@@ -59,14 +60,20 @@ void default_tile(int m, int64_t n, int64_t k, int cus, int *r, int *u, int *wav
         *waves = steps < 8 && (many || (steps == 1 && n >= kShortRowBlockMinRows))
                      ? kShortRowWaves
                      : 1;
-        if (steps > 8)
+        const int64_t per_cu = ceil_div(n, (int64_t)cus);   // one row per wave
+        if (steps > 8) {
             *u = 4;
-        else if (steps <= 2)
+        } else if (!many) {
             *u = 2;
-        else if (steps <= 4 || n <= (int64_t)kOneRoundWavesPerCU * cus)
+            while (*u < 8 && *u < steps && per_cu * *u * kWaveStep * 2 < kBurstTargetBytes)
+                *u *= 2;
+        } else if (steps <= 2) {
+            *u = 2;
+        } else if (steps <= 4) {
             *u = 4;
-        else
+        } else {
             *u = 8;
+        }
     } else if (m == 2) {
         // 2 <= M <= 16: the tiles of the LDS-staged batch kernel (batch.hip), measured on
         // MI355X at 4096 x 14336; each is also a compiled tile of the general kernel, which

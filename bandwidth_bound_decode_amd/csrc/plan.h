@@ -43,6 +43,11 @@ constexpr int kOneRoundWavesPerCU = 16;   // short rows: up to this many waves p
 // within one round at 2-7 steps, 4096 x 1024..3584, between -4 % and +3 %, so those keep
 // single-wave workgroups, as do 1024 rows and K = 4096).
 constexpr int64_t kShortRowBlockMinRows = 2048;
+// Batch-1 grids of one round (at most kOneRoundWavesPerCU single-wave workgroups per CU)
+// take the shortest burst that keeps this many bytes in flight per CU: the read ceiling's
+// knee (measured on MI355X: K = 4096 at 1-4 waves per CU fastest with bursts of 8, at 6-8
+// with 4, at 12-16 with 2; e.g. 768 x 4096 3.10 -> 2.87 us, 4096 x 4096 6.75 -> 6.54 us).
+constexpr int64_t kBurstTargetBytes = 24 * 1024;
 constexpr int kShortRowWaves = 8;
                                           // as one round, uncapped
 // Ticket counters sit at the start of a split plan's workspace in a region of at least this

@@ -151,8 +151,12 @@ def test_bytes_in_flight_report():
 BATCH1_TILES = {
     (4096, 14336): (1, 4, 8),      # down_proj: 4096 one-row waves in two rounds of 8 per CU
     (4097, 14337): (1, 4, 6),      # 17 waves per CU: three rounds of at most 6, not 8+8+1
-    (4096, 4096): (1, 4, 0),       # o_proj: 16 waves per CU, one uncapped round
-    (1024, 4096): (1, 4, 0),       # k_proj
+    (4096, 4096): (1, 2, 0),       # o_proj: 16 waves per CU, one uncapped round, 32 KiB
+    (1024, 4096): (1, 8, 0),       # k_proj: 4 waves per CU, bursts of 8 for 32 KiB
+    (768, 4096): (1, 8, 0),        # one GPU's QKV share at G = 8: 3 waves per CU
+    (1536, 4096): (1, 4, 0),       # 6 waves per CU: 24 KiB at bursts of 4
+    (3584, 4096): (1, 2, 0),       # 14 waves per CU
+    (4096, 2048): (1, 2, 0),       # rows of 4 steps, 16 waves per CU
     (6144, 4096): (1, 8, 12),      # QKV: 24 waves per CU in two rounds of 12
     (28672, 4096): (1, 8, 12),     # gate_up
     (128256, 4096): (1, 8, 12),    # LM head: 501 waves per CU in 42 rounds of at most 12
