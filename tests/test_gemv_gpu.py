@@ -327,8 +327,8 @@ def test_large_x_stride():
 
 
 def test_a_million_rows():
-    """N = 2^20 short rows: a million single-wave workgroups at batch 1, and 32,768 matrix-core
-    blocks at batch 16, checked in full."""
+    """N = 2^20 short rows: 131,072 eight-wave workgroups (one row per wave) at batch 1, and
+    32,768 matrix-core blocks at batch 16, checked in full."""
     n, k = 1 << 20, 64
     for m in (1, 16):
         w, x = draw(n, k, m, seed=m)
@@ -336,6 +336,21 @@ def test_a_million_rows():
         Y, p = gemv(W, X)
         print(m, p.info, flush=True)
         oracle_check(W, X, Y, f"n=2^20 m={m}")
+
+
+@pytest.mark.parametrize("n,k", [(4096, 512), (8200, 1000), (5000, 3000), (9000, 3583)])
+def test_short_rows_in_multi_wave_workgroups(n, k):
+    """Batch-1 rows under 8 wave steps in numbers run in 8-wave workgroups: every output
+    against the oracle, and bitwise equal to single-wave workgroups (each row is summed in
+    the same order whatever the workgroup)."""
+    w, x = draw(n, k, 1, seed=n + k)
+    W, X = device_matrix(w), device_matrix(x)
+    Y, p = gemv(W, X)
+    assert p.info["waves_per_block"] == 8, p.info
+    oracle_check(W, X, Y, f"{n}x{k} in 8-wave workgroups")
+    Y1, p1 = gemv(W, X, waves_per_block=1)
+    assert p1.info["waves_per_block"] == 1 and p1.info["splits"] == p.info["splits"]
+    assert bits_equal(Y, Y1), "8-wave and single-wave workgroups differ"
 
 
 def test_device_plans_equal_host_plans():
