@@ -327,7 +327,7 @@ def test_int4_plans():
         (2, 2, 4, 2048)
     assert lm["int4_fp16"] == 1
     q = plan(6144, 4096, weights="int4").info
-    assert (q["rows_per_wave"], q["unroll"], q["waves_per_block"], q["grid_x"]) == (1, 2, 8, 768)
+    assert (q["rows_per_wave"], q["unroll"], q["waves_per_block"], q["grid_x"]) == (1, 2, 4, 1536)
     assert plan(6144, 4096, weights="int4", int4_fp16=1).info["int4_fp16"] == 1
     assert plan(128256, 4096, weights="int4", int4_fp16=-1).info["int4_fp16"] == 0
     with pytest.raises(bbd.GemvError):
