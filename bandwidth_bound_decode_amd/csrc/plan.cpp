@@ -492,6 +492,8 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
                     break;
             }
             mf = mf_depth <= kMaxDepth;
+            if (mf && mf_s > 1 && o.mfma == 0 && (int64_t)m * k <= kMfmaSplitMinMK)
+                mf = 0;   // a split this small runs faster on the VALU kernels
         }
     }
 

@@ -75,6 +75,12 @@ constexpr int kMfmaNarrowChunk = 128;
 constexpr int kMfmaNarrowShortX = 8;                    // X vectors staged for M <= 8
 constexpr int64_t kMfmaNarrowMaxMK = 14 * 14336;
 constexpr int kMfmaWaves = 8;
+// An automatic matrix-core plan that has to split K (too few row blocks for the CUs) gives
+// way to the VALU kernels up to this M K: the split's combine is then most of the time
+// (measured on MI355X: 1024 x 4096 at M = 2 / 4 4.39 / 5.80 us on the VALU kernels against
+// 6.43 / 6.58 us split; 2048 and 3072 x 4096 the same; M = 8 at K = 4096, or M = 4 at
+// K = 14336 (12.1 against 15.0 us at 2048 rows), stay on the matrix cores).
+constexpr int64_t kMfmaSplitMinMK = 16384;
 constexpr int kMfmaMinBatch = 2;
 // INT4 weights (int4.hip): 32 weights per 16-byte vector, one bf16 scale per 128.
 constexpr int kInt4VecElems = 32;

@@ -298,6 +298,13 @@ def test_mfma_plans():
     small8 = plan(33, 4096, 8).info                           # 3 narrow blocks: the same
     assert small8["mfma_rows"] == 16 and small8["mfma_grid_x"] == 3
     assert small8["mfma_splits"] == 4096 // 1024 and small8["mfma_slice"] == 1024
+    # a split matrix-core plan with M K <= 16384 gives way to the VALU kernels
+    assert plan(1024, 4096, 2).info["mfma"] == 0              # 64 blocks: would split by 4
+    assert plan(3072, 4096, 4).info["mfma"] == 0
+    assert plan(1024, 4096, 8).info["mfma"] == 1
+    assert plan(2048, 14336, 2).info["mfma"] == 1
+    assert plan(4096, 4096, 2).info["mfma"] == 1              # 256 blocks: no split
+    assert plan(1024, 4096, 2, mfma=1).info["mfma"] == 1
     long_k = plan(64, 1 << 19, 16).info                       # accuracy forces the split
     assert long_k["mfma"] == 1 and long_k["mfma_depth_bound"] <= 160
     with pytest.raises(bbd.GemvError):
