@@ -4,9 +4,8 @@
 // v_dot2 instructions, so their time grows with M (about 0.6 us per extra vector at
 // 4096 x 14336: 19.9 us at M = 2, 24.4 at 8, 28.3 at 16). Here one v_mfma_f32_16x16x32_bf16
 // takes 16 weight rows (A operand) and 16 input vectors (B operand) over 32 K elements, so
-// the arithmetic per weight byte does not grow with M (19.5 us at M = 2, 19.8 at 8). Batches
-// below 16 cycle through their vectors again in the unused B columns, whose outputs are
-// never stored.
+// the arithmetic per weight byte does not grow with M (19.3 us at M = 2, 19.8 at 8). Batches
+// below 16 repeat vectors in the unused B columns, whose outputs are never stored.
 //
 // Operand layout of the 16x16x32 bf16 MFMA on gfx950 (checked on the device against an
 // exact integer product): lane l holds A[l % 16][8 (l / 16) .. +8) and B[8 (l / 16) .. +8)
@@ -76,9 +75,8 @@ __device__ __forceinline__ floatx4 mfma(u32x4 a, u32x4 b, floatx4 c)
 // y[m][row] = sum_k w[row][k] x[m][k] for the row block blockIdx.x (T 16-row tiles) and
 // the K slice blockIdx.y (of gridDim.y), in chunks of CH elements. XV: X vectors staged
 // per chunk (16, or 8 when M <= 8: B lanes 8..15 then repeat vectors 0..7, and their
-// output columns are never stored). Slots past M take vector slot % M: repeating only
-// vector M - 1 put up to 7 of a load's 8 rows on one line, which cost about 5 % at M = 2
-// (4096 x 14336: 20.4 against 19.5 us). With one slice the result goes to y; with several,
+// output columns are never stored; vectors past M repeat vector M - 1, whose lines the
+// memory system then fetches once). With one slice the result goes to y; with several,
 // to partial[slice][m][row] and then, by the last arrival, to y.
 template <int T, int XV, int CH>
 __global__ void __launch_bounds__(kThreads)
@@ -113,8 +111,8 @@ __global__ void __launch_bounds__(kThreads)
         gw[j] = w + (int64_t)min(row0 + kLineRows * j + lr, n - 1) * ldw + k0 + 8 * lq;
     const uint16_t *gx[kXGroups];
 #pragma unroll
-    for (int j = 0; j < kXGroups; ++j)   // vectors past M cycle through 0..M-1
-        gx[j] = x + (int64_t)((kLineRows * j + lr) % m) * ldx + k0 + 8 * lq;
+    for (int j = 0; j < kXGroups; ++j)   // vectors past M repeat the last one
+        gx[j] = x + (int64_t)min(kLineRows * j + lr, m - 1) * ldx + k0 + 8 * lq;
     // Read side: operand lane (i16, g) of MFMA u takes piece 4 (u % 2) + g of line u / 2 of
     // row i16, which group i16 / 8 (of its tile, or of X) left in slot
     // 8 (i16 % 8) + ((4 (u % 2) + g) ^ (i16 % 8)).
