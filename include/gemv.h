@@ -72,7 +72,10 @@ typedef struct gemv_plan_s *gemv_plan_t;
  *   mfma            the matrix-core kernel for batches (decode-GEMV page: past a handful of
  *                   vectors the work stops being a matrix-vector product and matrix units
  *                   start to pay; on MI355X they do from M = 2): 0 = automatic (M >= 2
- *                   with no tile, split or cap forced), 1 = for any M >= 2, -1 = never. It
+ *                   with no tile, split or cap forced, except where the matrix-core launch
+ *                   would have to split K and M*K <= 16384: there the split's combine costs
+ *                   more than the VALU kernels' extra vectors), 1 = for any M >= 2,
+ *                   -1 = never. It
  *                   needs K to be a multiple of 64 (of 128 for the 16-row form).
  *                   It runs only for 16-byte-aligned single-matrix calls; other calls of
  *                   the same plan take the VALU kernels the fields above describe. The
