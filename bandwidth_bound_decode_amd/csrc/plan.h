@@ -49,14 +49,13 @@ constexpr int64_t kShortRowBlockMinRows = 2048;
 // with 4, at 12-16 with 2; e.g. 768 x 4096 3.10 -> 2.87 us, 4096 x 4096 6.75 -> 6.54 us).
 constexpr int64_t kBurstTargetBytes = 24 * 1024;
 constexpr int kShortRowWaves = 8;
-                                          // as one round, uncapped
 // Ticket counters sit at the start of a split plan's workspace in a region of at least this
 // many slots, so that plans with up to this many row blocks can share one workspace in any
 // order without one plan's partial sums landing on another plan's tickets.
 constexpr int64_t kTicketSlots = 4096;
 // Matrix-core kernel (mfma.hip): workgroups of 8 waves that take K in chunks; used by
 // default from this batch size on (at 4096 x 14336 it is faster than the VALU kernels from
-// M = 2 on: 19.3 against 19.9 us, and 19.8 against 24.4 us at M = 8). Two forms: 32-row
+// M = 2 on: 19.4 against 19.8 us, and 19.8 against 24.4 us at M = 8). Two forms: 32-row
 // blocks with 64-element chunks, whose two 16-row tiles share every X fragment, and 16-row
 // blocks with 128-element chunks, twice the row blocks (4096 rows fill 256 CUs without
 // splitting K). The 16-row form is taken (K a multiple of 128) for M <= 8, where it stages
@@ -77,9 +76,10 @@ constexpr int64_t kMfmaNarrowMaxMK = 14 * 14336;
 constexpr int kMfmaWaves = 8;
 // An automatic matrix-core plan that has to split K (too few row blocks for the CUs) gives
 // way to the VALU kernels up to this M K: the split's combine is then most of the time
-// (measured on MI355X: 1024 x 4096 at M = 2 / 4 4.39 / 5.80 us on the VALU kernels against
-// 6.43 / 6.58 us split; 2048 and 3072 x 4096 the same; M = 8 at K = 4096, or M = 4 at
-// K = 14336 (12.1 against 15.0 us at 2048 rows), stay on the matrix cores).
+// (measured on MI355X, each shape warmed up: at M = 2 / 4, 1024 x 4096 4.39 / 5.80 us on the
+// VALU kernels against 6.43 / 6.58 us split, 2048 x 4096 5.39 / 6.40 against 6.95 / 7.13 us,
+// 3072 x 4096 6.77 / 7.80 against 8.85 / 9.01 us; M = 8 at K = 4096 (7.18 against 7.92 us
+// at 2048 rows) and M = 4 at K = 14336 (12.0 against 14.9 us) stay on the matrix cores).
 constexpr int64_t kMfmaSplitMinMK = 16384;
 constexpr int kMfmaMinBatch = 2;
 // INT4 weights (int4.hip): 32 weights per 16-byte vector, one bf16 scale per 128.
