@@ -63,7 +63,8 @@ class PlanInfo(ctypes.Structure):
                 ("mfma_splits", ctypes.c_int), ("mfma_slice", ctypes.c_int64),
                 ("mfma_grid_x", ctypes.c_int), ("mfma_depth_bound", ctypes.c_int),
                 ("weights", ctypes.c_int), ("prologue", ctypes.c_int),
-                ("int4_fp16", ctypes.c_int), ("mfma_rows", ctypes.c_int)]
+                ("int4_fp16", ctypes.c_int), ("mfma_rows", ctypes.c_int),
+                ("mfma_unaligned_depth", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

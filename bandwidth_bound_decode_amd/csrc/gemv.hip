@@ -1020,6 +1020,9 @@ gemv_status launch_on(gemv_plan_t p, const gemv_segment *segs, int nseg, const v
     if (done || st != GEMV_OK)
         return st;
     if (!fast && nseg == 1) {
+        st = bbd::launch_mfma_unaligned(p, segs[0], X, ldx, stream, &done);
+        if (done || st != GEMV_OK)
+            return st;
         st = launch_unaligned_lds(p, segs[0], X, ldx, stream, &done);
         if (done || st != GEMV_OK)
             return st;

@@ -47,6 +47,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "plan.h"
 
@@ -56,6 +58,7 @@ using namespace bbd;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -231,6 +234,235 @@ __global__ void __launch_bounds__(kThreads)
         __hip_atomic_store(tickets + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Unaligned rows (W rows or x rows not on the 16-byte grid) on the matrix cores, for larger
+// batches, where the VALU kernels' work per weight grows with M. Rows c, c + C, c + 2C, ...
+// (C = 8 / gcd(ldw, 8) classes) start at the same offset h from the 16-byte grid, so each
+// class is an aligned matrix: base w + c ldw + h, row stride C ldw (a multiple of 8
+// elements). A workgroup owns one 16-row tile of one class; the 1-D grid lists the tiles
+// every class has first (class fastest), then each class's remaining tiles. Within a tile:
+//   - the 8 waves take the class rows' whole 128-element chunks in turn from a
+//     per-workgroup rotation and stream them through a private LDS buffer as the aligned
+//     kernel does (direct loads of 8 rows x 128 bytes, streaming hint, XOR-swizzled slots;
+//     rows past the class end are not loaded and never stored);
+//   - B comes from x in registers: for x row i16 at K element e, one 4-byte-aligned 16-byte
+//     load and one dword give 9 dwords, and v_alignbyte by the row's 2-byte phase picks the
+//     8 elements starting at e. These loads go out with the chunk's W lines;
+//   - chunks whose x window would leave the row (the first when h = 0: the window starts
+//     one element early; the last one or two) and the ragged end take one wave each, with
+//     W loaded in the operand layout and x element by element, before the stream;
+//   - the h head elements and the < 8 tail elements past the last whole vector are summed
+//     per (x row, tile row) pair in fp32 by one thread each and added after the waves' sums.
+// The order of every sum is fixed: bitwise reproducible, within the VALU kernels' tolerance
+// (another summation order).
+constexpr int kUnalChunk = 128;
+
+__global__ void __launch_bounds__(kThreads)
+    gemv_mfma_unaligned(const uint16_t *w, const uint16_t *x, float *y, int n, int k, int ldw,
+                        int ldx, int ldy, int m, int classes)
+{
+    constexpr int CH = kUnalChunk;
+    constexpr int kLines = CH / kLineElems, kU = CH / 32, kWLoads = 2 * kLines;
+    __shared__ floatx4 red[kMfmaWaves - 1][kWaveLanes];
+    __shared__ u32x4 stage[kMfmaWaves][kWLoads][kWaveLanes];
+    __shared__ float edge_sums[16 * 16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int i16 = lane & 15, g = lane >> 4;
+
+    // This workgroup's class and first class row.
+    int cls = -1, j0 = 0;
+    {
+        const int id = blockIdx.x;
+        const int common = n / classes / 16;   // whole tiles every class has
+        if (id < common * classes) {
+            cls = id % classes;
+            j0 = id / classes * 16;
+        } else {
+            int r = id - common * classes;
+            for (int c = 0; c < classes; ++c) {
+                const int extra = ((n - c + classes - 1) / classes + 15) / 16 - common;
+                if (r < extra) {
+                    cls = c;
+                    j0 = (common + r) * 16;
+                    break;
+                }
+                r -= extra;
+            }
+        }
+    }
+    if (cls < 0)
+        return;   // not reached with the launch's grid (the tile count)
+    const int crows = (n - cls + classes - 1) / classes;
+    const uint16_t *wc = w + (int64_t)cls * ldw;
+    const int64_t cs = (int64_t)classes * ldw;
+    const int h = (int)((8u - (unsigned)(((uintptr_t)wc >> 1) & 7u)) & 7u);
+    const int ka = min(h, k);                                   // head elements
+    const int nvec = ka + 8 <= k ? (k - ka) >> 3 : 0;           // aligned 8-element vectors
+    const uint16_t *wb = wc + ka;
+    const int full = nvec * 8 / CH;                             // whole chunks
+    const int total = (nvec * 8 + CH - 1) / CH;                 // with the ragged one
+    const int c_lo = ka == 0 && full > 0 ? 1 : 0;
+    int c_hi = full;
+    while (c_hi > c_lo && ka + c_hi * CH + 2 > k)
+        --c_hi;
+    const int dma = c_hi - c_lo;                                // streamed chunks
+
+    // Load side of the stream: row lr of each 8-row group, piece lq of each line.
+    const int lr = lane >> 3, lq = (lane & 7) ^ lr;
+    const uint16_t *gw[2];
+    bool gv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        gv[j] = j0 + 8 * j + lr < crows;
+        gw[j] = wb + (int64_t)min(j0 + 8 * j + lr, crows - 1) * cs + 8 * lq;
+    }
+    const int ri = i16 & 7, hj = i16 >> 3;
+    int slot[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        slot[q] = kLineRows * ri + ((4 * q + g) ^ ri);
+    u32x4 (&buf)[kWLoads][kWaveLanes] = stage[wave];
+
+    // B side: x row i16 (past M the last row; those columns are never stored).
+    const uint16_t *xb = x + (int64_t)min(i16, m - 1) * ldx;
+    const unsigned phase = (unsigned)((((uintptr_t)xb >> 1) + (unsigned)ka) & 1u);
+    const unsigned sh = phase * 2u;
+    const uint16_t *xw = xb + ka - (int)phase;   // 4-byte aligned
+
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int turns = dma > wave ? (dma - wave + kMfmaWaves - 1) / kMfmaWaves : 0;
+    const int rot = dma > 0 ? (int)((blockIdx.x * 37u + (unsigned)cls * 11u) % (unsigned)dma) : 0;
+    u32x4 xa[2][kU];
+    unsigned xe[2][kU];
+    auto issue = [&](int i, int sb) {
+        int c = wave + i * kMfmaWaves + rot;
+        c = (c >= dma ? c - dma : c) + c_lo;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (gv[j]) {
+#pragma unroll
+                for (int l = 0; l < kLines; ++l)
+                    __builtin_amdgcn_global_load_lds(
+                        (global_void *)(gw[j] + c * CH + kLineElems * l),
+                        (lds_void *)&buf[j * kLines + l][0], 16, 0, kCachePolicyNT);
+            }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const unsigned *d = reinterpret_cast<const unsigned *>(xw + c * CH + 32 * u + 8 * g);
+            xa[sb][u] = *reinterpret_cast<const u32x4_a4 *>(d);
+            xe[sb][u] = d[4];
+        }
+    };
+
+    // Head and tail elements of pair p = (x row p / 16, tile row p % 16); indices clamped,
+    // products past the ends dropped.
+    const int tail_begin = ka + 8 * nvec;
+    const int pidx = wave * kWaveLanes + lane;
+    const int pr = pidx & 15, pm = min(pidx >> 4, m - 1);
+    const uint16_t *hw = wc + (int64_t)min(j0 + pr, crows - 1) * cs;
+    const uint16_t *hx = x + (int64_t)pm * ldx;
+    unsigned short hwv[16], hxv[16];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int kh = min(e, k - 1), kt = min(tail_begin + e, k - 1);
+        hwv[e] = hw[kh];
+        hxv[e] = hx[kh];
+        hwv[8 + e] = hw[kt];
+        hxv[8 + e] = hx[kt];
+    }
+    // The edge and ragged chunks ([0, c_lo) and [c_hi, total), at most 3), one per wave.
+    const int nrest = c_lo + (total - c_hi);
+    const bool rest = wave < nrest;
+    const int rc = wave < c_lo ? wave : c_hi + (wave - c_lo);
+    u32x4 ra[kU], rb[kU];
+    if (rest) {
+        const uint16_t *wa = wb + (int64_t)min(j0 + i16, crows - 1) * cs;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int vc = min(rc * (CH / 8) + 4 * u + g, nvec - 1);
+            ra[u] = load_stream(wa + 8 * vc);
+            const uint16_t *xv = xb + ka + 8 * vc;
+            rb[u].x = (unsigned)xv[0] | ((unsigned)xv[1] << 16);
+            rb[u].y = (unsigned)xv[2] | ((unsigned)xv[3] << 16);
+            rb[u].z = (unsigned)xv[4] | ((unsigned)xv[5] << 16);
+            rb[u].w = (unsigned)xv[6] | ((unsigned)xv[7] << 16);
+        }
+    }
+    if (turns > 0)
+        issue(0, 0);
+    if (rest) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int v = rc * (CH / 8) + 4 * u + g;
+            const u32x4 z = {0, 0, 0, 0};
+            acc = mfma(v < nvec ? ra[u] : z, rb[u], acc);
+        }
+    }
+    {
+        float es = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e < ka)
+                es = fmaf(__uint_as_float((unsigned)hwv[e] << 16),
+                          __uint_as_float((unsigned)hxv[e] << 16), es);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (tail_begin + e < k)
+                es = fmaf(__uint_as_float((unsigned)hwv[8 + e] << 16),
+                          __uint_as_float((unsigned)hxv[8 + e] << 16), es);
+        if (pidx < 16 * 16)
+            edge_sums[pidx] = es;
+    }
+    // The stream: per chunk the wait for its W lines and x windows, the LDS operand reads,
+    // the next chunk's loads (into the other x registers), then the MFMAs.
+    auto step = [&](int i, auto sbc) {
+        constexpr int sb = decltype(sbc)::value;
+        __builtin_amdgcn_s_waitcnt(kWaitVmOnly);
+        u32x4 a[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            a[u] = buf[hj * kLines + u / 2][slot[u & 1]];
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmOnly);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < turns)
+            issue(i + 1, 1 - sb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const u32x4 r = xa[sb][u];
+            u32x4 b;
+            b.x = __builtin_amdgcn_alignbyte(r.y, r.x, sh);
+            b.y = __builtin_amdgcn_alignbyte(r.z, r.y, sh);
+            b.z = __builtin_amdgcn_alignbyte(r.w, r.z, sh);
+            b.w = __builtin_amdgcn_alignbyte(xe[sb][u], r.w, sh);
+            acc = mfma(a[u], b, acc);
+        }
+    };
+    for (int i = 0; i < turns; i += 2) {
+        step(i, std::integral_constant<int, 0>{});
+        if (i + 1 < turns)
+            step(i + 1, std::integral_constant<int, 1>{});
+    }
+
+    if (wave > 0)
+        red[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave != 0)
+        return;
+#pragma unroll
+    for (int v = 0; v < kMfmaWaves - 1; ++v)
+        acc += red[v][lane];
+    if (i16 < m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + 4 * g + e;
+            if (j < crows)
+                y[(int64_t)i16 * ldy + cls + (int64_t)classes * j] =
+                    acc[e] + edge_sums[i16 * 16 + 4 * g + e];
+        }
+    }
+}
+
 }  // namespace
 
 namespace bbd {
@@ -268,6 +500,31 @@ gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const
     hipError_t e = hipLaunchKernel(fn,
                                    dim3((unsigned)p->mfma_grid_x, (unsigned)p->mfma_splits),
                                    dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMV_OK : record_hip_error((int)e, GEMV_ERR_DEVICE);
+}
+
+gemv_status launch_mfma_unaligned(gemv_plan_t p, const gemv_segment &seg, const void *X,
+                                  int64_t ldx, void *stream, bool *done)
+{
+    *done = false;
+    if (!p->mfma_unaligned_depth)
+        return GEMV_OK;
+    // Rows r and r + classes start at the same offset from the 16-byte grid.
+    const int r8 = (int)(seg.ldw % 8);
+    const int classes = r8 == 0 ? 1 : r8 % 4 == 0 ? 2 : r8 % 2 == 0 ? 4 : 8;
+    int64_t tiles = 0;
+    for (int c = 0; c < classes; ++c)
+        tiles += ((p->n - c + classes - 1) / classes + 15) / 16;
+    *done = true;
+    const uint16_t *w = static_cast<const uint16_t *>(seg.W);
+    const uint16_t *x = static_cast<const uint16_t *>(X);
+    float *y = seg.Y;
+    int n = (int)p->n, k = (int)p->k, ldw = (int)seg.ldw, ldxi = (int)ldx, ldy = (int)seg.ldy,
+        m = p->m, cl = classes;
+    void *args[] = {&w, &x, &y, &n, &k, &ldw, &ldxi, &ldy, &m, &cl};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemv_mfma_unaligned),
+                                   dim3((unsigned)tiles), dim3(kThreads), args, 0,
+                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GEMV_OK : record_hip_error((int)e, GEMV_ERR_DEVICE);
 }
 

@@ -159,6 +159,17 @@ int mfma_depth_for(int64_t slice, int s, int chunk)
     return (int)(32 + (chunk / 32) * turns + (kMfmaWaves - 1) + (s - 1));
 }
 
+// The matrix-core kernel for unaligned rows: a wave's chain holds the MFMAs of at most one
+// edge or ragged chunk and of its share of the streamed whole chunks (32 roundings in the
+// first MFMA, then one per MFMA), then the 7 wave additions, then the addition of the fp32
+// sum of the <= 15 head and tail elements (a shorter chain).
+int mfma_unaligned_depth_for(int64_t k)
+{
+    const int64_t chunks = k / kMfmaUnalignedChunk;
+    const int64_t turns = ceil_div(chunks, kMfmaWaves) + 1;
+    return (int)(32 + (kMfmaUnalignedChunk / 32) * turns + (kMfmaWaves - 1) + 1);
+}
+
 bool valid_waves(int w) { return w == 1 || w == 2 || w == 4 || w == 8; }
 
 // INT4 weights, unsplit. A product of a 32-weight vector passes through its 16-step dot2
@@ -497,6 +508,20 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
         }
     }
 
+    // Unaligned single-matrix calls on the matrix cores (decided per call: the layout is
+    // the call's): from kMfmaUnalignedMinBatch by default, with every tile option left to
+    // the plan, rows enough for the CUs and the kernel's chain within the depth bound.
+    int mf_unal = 0;
+    {
+        const bool forced = o.splits || o.rows_per_wave || o.waves_per_block || o.unroll ||
+                            o.waves_per_cu;
+        const bool want = o.mfma > 0 ? m >= 2 : o.mfma == 0 && m >= kMfmaUnalignedMinBatch && !forced;
+        const int depth = mfma_unaligned_depth_for(k);
+        if (want && n >= (int64_t)kMfmaUnalignedRowsPerCU * dev->compute_units &&
+            depth <= kMaxDepth)
+            mf_unal = depth;
+    }
+
     gemv_plan_s *p = new (std::nothrow) gemv_plan_s;
     if (!p)
         return GEMV_ERR_INVALID_ARG;
@@ -507,6 +532,7 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     p->device = -1;
     p->dev = *dev;
     p->splits = s;
+    p->mfma_unaligned_depth = mf_unal;
     p->rows_per_wave = r;
     p->waves_per_block = waves;
     p->unroll = u;
@@ -575,6 +601,7 @@ extern "C" gemv_status gemv_plan_query(gemv_plan_t p, gemv_plan_info *info)
     info->weights = p->weights;
     info->prologue = p->prologue;
     info->int4_fp16 = p->int4_fp16;
+    info->mfma_unaligned_depth = p->mfma_unaligned_depth;
     return GEMV_OK;
 }
 

@@ -82,6 +82,14 @@ constexpr int kMfmaWaves = 8;
 // at 2048 rows) and M = 4 at K = 14336 (12.0 against 14.9 us) stay on the matrix cores).
 constexpr int64_t kMfmaSplitMinMK = 16384;
 constexpr int kMfmaMinBatch = 2;
+// Unaligned single-matrix calls (W or x rows off the 16-byte grid) run on the matrix cores
+// from this batch size (measured on MI355X at 4097 x 14337, odd row stride, against the
+// class-staged VALU kernel: M = 12 50.1 against 50.8 us, 13 51.3 against 54.6, 14 52.4
+// against 64.1, 16 54.9 against 67.4; M = 8 43.9 against 38.8 us), with at least
+// kMfmaUnalignedRowsPerCU rows per CU so that its 16-row tiles cover the CUs.
+constexpr int kMfmaUnalignedMinBatch = 13;
+constexpr int kMfmaUnalignedRowsPerCU = 16;
+constexpr int kMfmaUnalignedChunk = 128;
 // INT4 weights (int4.hip): 32 weights per 16-byte vector, one bf16 scale per 128.
 constexpr int kInt4VecElems = 32;
 constexpr int kInt4Group = 128;
@@ -131,6 +139,11 @@ gemv_status launch_mfma(gemv_plan_t p, const gemv_segment *segs, int nseg, const
                         int64_t ldx, unsigned *tickets, float *partial, void *stream,
                         bool *done);
 
+// Launch a validated unaligned single-matrix call on the matrix-core kernel for unaligned
+// rows (mfma.hip) when the plan allows it; *done tells whether it did.
+gemv_status launch_mfma_unaligned(gemv_plan_t p, const gemv_segment &seg, const void *X,
+                                  int64_t ldx, void *stream, bool *done);
+
 // RMSNorm-prologue launch (norm.hip) of a validated call; the plan's unroll picks the kernel.
 gemv_status launch_rmsnorm(gemv_plan_t p, const gemv_segment *segs, int nseg, const void *H,
                            const void *gamma, float eps, void *stream);
@@ -175,4 +188,5 @@ struct gemv_plan_s {
     int weights;                // GEMV_WEIGHTS_BF16 or GEMV_WEIGHTS_INT4
     int prologue;               // 0 or GEMV_PROLOGUE_RMSNORM
     int int4_fp16;              // INT4 with x in LDS: the workgroups try the fp16 staging
+    int mfma_unaligned_depth;   // unaligned single-matrix calls run on the matrix cores (> 0)
 };

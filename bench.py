@@ -853,9 +853,14 @@ def main(argv=None):
             info = r["plan"]
             r["plan"] = {k: info[k] for k in ("splits", "rows_per_wave", "unroll",
                                               "grid_x", "grid_y")}
-            if gg.k % 8 and not segs and info["splits"] == 1:
-                # contiguous rows of odd length sit at 2-byte offsets: the call takes the
-                # class-staged unaligned kernel, whose wave shape is its own (not the plan's)
+            if gg.k % 8 and not segs and info["mfma_unaligned_depth"]:
+                # contiguous rows of odd length sit at 2-byte offsets; from M = 13 such calls
+                # run on the matrix cores in 16-row tiles of each row class
+                r["plan"] = {"kernel": "gemv_mfma_unaligned", "splits": 1,
+                             "classes": 8, "rows_per_block": 16}
+            elif gg.k % 8 and not segs and info["splits"] == 1:
+                # below that the class-staged unaligned kernel, whose wave shape is its own
+                # (not the plan's)
                 r["plan"] = {"kernel": "gemv_unaligned_lds", "splits": 1}
             elif info["mfma"]:    # aligned calls of this plan run the matrix-core kernel
                 r["plan"] = {"kernel": "gemv_mfma", "splits": info["mfma_splits"],

@@ -3,7 +3,10 @@ vectors for M <= 8, 16-row blocks staging 16 for larger M where 32-row blocks wo
 32-row blocks otherwise): within tolerance of the oracle at the down_proj shape and on small
 shapes that span several row blocks with a ragged last one,
 unsplit and split over K; exact where every partial sum is exact (identity, one-hot, constant
-W); reproducible bit for bit; and the unaligned fallback equal to the VALU plan."""
+W); reproducible bit for bit; unaligned calls with too few rows for the matrix-core form
+of unaligned rows equal to the VALU plan; and that form itself (row classes of every
+size, x at either 2-byte phase, edge-only and head-and-tail-only rows, the longest K its
+depth bound allows) within tolerance of the oracle, reproducible, and not the VALU run."""
 import numpy as np
 import pytest
 import torch
@@ -135,3 +138,38 @@ def test_unaligned_call_takes_the_valu_kernels():
     oracle_check(W, X, Y, "unaligned fallback")
     Yv, _ = gemv(W, X, mfma=-1)
     assert bits_equal(Y, Yv), "fallback differs from the VALU plan"
+
+
+# n, k, m, ldw, W offset, ldx, X offset (elements): 8 / gcd(ldw, 8) row classes, x phases
+UNALIGNED = [
+    (4097, 14337, 16, 14337, 0, 14340, 1),   # 8 classes, class 0 one row past its tiles
+    (4097, 14337, 13, 14337, 1, 14337, 0),   # x rows at alternating 2-byte phases
+    (4100, 2000, 16, 2002, 1, 2005, 2),      # 4 classes
+    (4160, 1024, 14, 1028, 3, 1024, 0),      # 2 classes, x on the grid
+    (4096, 4096, 16, 4096, 1, 4096, 0),      # 1 class, every row 7 elements off the grid
+    (4096, 4096, 15, 4096, 0, 4096, 1),      # W on the grid, x off it: first chunk apart
+    (4099, 100, 16, 101, 1, 103, 1),         # no whole chunk: edge and ragged chunks only
+    (4096, 13, 16, 13, 1, 13, 0),            # head and tail elements only
+    (4096, 29000, 13, 29001, 1, 29003, 1),   # depth bound 160, the longest allowed
+]
+
+
+@pytest.mark.parametrize("n,k,m,ldw,woff,ldx,xoff", UNALIGNED)
+def test_unaligned_rows_on_the_matrix_cores(n, k, m, ldw, woff, ldx, xoff):
+    """Rows off the 16-byte grid, M >= 13 by default: the class-tiled matrix-core kernel."""
+    what = f"unaligned mfma n={n} k={k} m={m} ldw={ldw} offsets {woff}/{xoff}"
+    print(what, flush=True)
+    w, x = draw(n, k, m, seed=n + k + m)
+    W = device_matrix(w, ld=ldw, offset=woff)
+    X = device_matrix(x, ld=ldx, offset=xoff)
+    p = bbd.Plan(n, k, m)
+    assert 0 < p.info["mfma_unaligned_depth"] <= 160, p.info
+    Y, _ = gemv(W, X, plan=p)
+    oracle_check(W, X, Y, what)
+    Y2, _ = gemv(W, X, plan=p)
+    assert bits_equal(Y, Y2), "not reproducible"
+    Yv, pv = gemv(W, X, mfma=-1)
+    assert pv.info["mfma_unaligned_depth"] == 0
+    oracle_check(W, X, Yv, what + " (VALU)")
+    if k >= 1024:   # another summation order: some outputs round differently
+        assert not bits_equal(Y, Yv), "the matrix-core kernel did not run"

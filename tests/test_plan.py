@@ -305,6 +305,18 @@ def test_mfma_plans():
     assert plan(2048, 14336, 2).info["mfma"] == 1
     assert plan(4096, 4096, 2).info["mfma"] == 1              # 256 blocks: no split
     assert plan(1024, 4096, 2, mfma=1).info["mfma"] == 1
+    # unaligned calls on the matrix cores: M >= 13 by default, rows enough for the CUs
+    u16 = plan(4097, 14337, 16).info
+    assert u16["mfma"] == 0 and u16["mfma_unaligned_depth"] == 32 + 4 * (14 + 1) + 7 + 1
+    assert plan(4097, 14337, 13).info["mfma_unaligned_depth"] > 0
+    assert plan(4097, 14337, 12).info["mfma_unaligned_depth"] == 0
+    assert plan(4097, 14337, 3, mfma=1).info["mfma_unaligned_depth"] > 0
+    assert plan(4097, 14337, 16, mfma=-1).info["mfma_unaligned_depth"] == 0
+    assert plan(4097, 14337, 16, unroll=2).info["mfma_unaligned_depth"] == 0
+    assert plan(4095, 14337, 16).info["mfma_unaligned_depth"] == 0   # < 16 rows per CU
+    assert plan(4096, 29823, 16).info["mfma_unaligned_depth"] == 160  # the longest row
+    assert plan(4096, 29824, 16).info["mfma_unaligned_depth"] == 0
+    assert plan(4097, 14337, 1).info["mfma_unaligned_depth"] == 0
     long_k = plan(64, 1 << 19, 16).info                       # accuracy forces the split
     assert long_k["mfma"] == 1 and long_k["mfma_depth_bound"] <= 160
     with pytest.raises(bbd.GemvError):
