@@ -83,11 +83,12 @@ constexpr int kMfmaWaves = 8;
 constexpr int64_t kMfmaSplitMinMK = 16384;
 constexpr int kMfmaMinBatch = 2;
 // Unaligned single-matrix calls (W or x rows off the 16-byte grid) run on the matrix cores
-// from this batch size (measured on MI355X at 4097 x 14337, odd row stride, against the
-// class-staged VALU kernel: M = 12 50.1 against 50.8 us, 13 51.3 against 54.6, 14 52.4
-// against 64.1, 16 54.9 against 67.4; M = 8 43.9 against 38.8 us), with at least
+// from this batch size (measured on MI355X against the class-staged VALU kernel, odd row
+// strides: 4097 x 14337 at M = 9 / 10 / 12 / 13 42.1 / 43.9 / 47.6 / 48.6 us against
+// 40.6 / 44.4 / 51.0 / 54.6, and 52.4 against 67.4 us at M = 16; 14337 x 4097 at M = 9 / 10
+// 39.8 / 41.3 against 40.1 / 43.0 us; 4099 x 4097 ahead from M = 8), with at least
 // kMfmaUnalignedRowsPerCU rows per CU so that its 16-row tiles cover the CUs.
-constexpr int kMfmaUnalignedMinBatch = 13;
+constexpr int kMfmaUnalignedMinBatch = 10;
 constexpr int kMfmaUnalignedRowsPerCU = 16;
 constexpr int kMfmaUnalignedChunk = 128;
 // INT4 weights (int4.hip): 32 weights per 16-byte vector, one bf16 scale per 128.

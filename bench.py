@@ -854,7 +854,7 @@ def main(argv=None):
             r["plan"] = {k: info[k] for k in ("splits", "rows_per_wave", "unroll",
                                               "grid_x", "grid_y")}
             if gg.k % 8 and not segs and info["mfma_unaligned_depth"]:
-                # contiguous rows of odd length sit at 2-byte offsets; from M = 13 such calls
+                # contiguous rows of odd length sit at 2-byte offsets; from M = 10 such calls
                 # run on the matrix cores in 16-row tiles of each row class
                 r["plan"] = {"kernel": "gemv_mfma_unaligned", "splits": 1,
                              "classes": 8, "rows_per_block": 16}

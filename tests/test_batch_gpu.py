@@ -87,7 +87,7 @@ def test_unaligned_tail_rows(n, m):
     rows) beside classes of 8, 135 rows one tail row in seven classes, 4097 one in class 0.
     Oracle parity and, since which rows are tail rows does not depend on M, every batch row
     bitwise equal to its batch-1 run; with x staged in chunks at M = 16 (the matrix cores,
-    which take such calls from M = 13 by default, switched off)."""
+    which take such calls from M = 10 by default, switched off)."""
     k = 2001 if m < 16 else 9001
     w, x = draw(n, k, m, seed=500 + n + m)
     W = device_matrix(w)                 # ldw = k, odd: every row at another 2-byte offset

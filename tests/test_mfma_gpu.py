@@ -143,7 +143,7 @@ def test_unaligned_call_takes_the_valu_kernels():
 # n, k, m, ldw, W offset, ldx, X offset (elements): 8 / gcd(ldw, 8) row classes, x phases
 UNALIGNED = [
     (4097, 14337, 16, 14337, 0, 14340, 1),   # 8 classes, class 0 one row past its tiles
-    (4097, 14337, 13, 14337, 1, 14337, 0),   # x rows at alternating 2-byte phases
+    (4097, 14337, 10, 14337, 1, 14337, 0),   # x rows at alternating 2-byte phases
     (4100, 2000, 16, 2002, 1, 2005, 2),      # 4 classes
     (4160, 1024, 14, 1028, 3, 1024, 0),      # 2 classes, x on the grid
     (4096, 4096, 16, 4096, 1, 4096, 0),      # 1 class, every row 7 elements off the grid
@@ -156,7 +156,7 @@ UNALIGNED = [
 
 @pytest.mark.parametrize("n,k,m,ldw,woff,ldx,xoff", UNALIGNED)
 def test_unaligned_rows_on_the_matrix_cores(n, k, m, ldw, woff, ldx, xoff):
-    """Rows off the 16-byte grid, M >= 13 by default: the class-tiled matrix-core kernel."""
+    """Rows off the 16-byte grid, M >= 10 by default: the class-tiled matrix-core kernel."""
     what = f"unaligned mfma n={n} k={k} m={m} ldw={ldw} offsets {woff}/{xoff}"
     print(what, flush=True)
     w, x = draw(n, k, m, seed=n + k + m)

@@ -305,11 +305,11 @@ def test_mfma_plans():
     assert plan(2048, 14336, 2).info["mfma"] == 1
     assert plan(4096, 4096, 2).info["mfma"] == 1              # 256 blocks: no split
     assert plan(1024, 4096, 2, mfma=1).info["mfma"] == 1
-    # unaligned calls on the matrix cores: M >= 13 by default, rows enough for the CUs
+    # unaligned calls on the matrix cores: M >= 10 by default, rows enough for the CUs
     u16 = plan(4097, 14337, 16).info
     assert u16["mfma"] == 0 and u16["mfma_unaligned_depth"] == 32 + 4 * (14 + 1) + 7 + 1
-    assert plan(4097, 14337, 13).info["mfma_unaligned_depth"] > 0
-    assert plan(4097, 14337, 12).info["mfma_unaligned_depth"] == 0
+    assert plan(4097, 14337, 10).info["mfma_unaligned_depth"] > 0
+    assert plan(4097, 14337, 9).info["mfma_unaligned_depth"] == 0
     assert plan(4097, 14337, 3, mfma=1).info["mfma_unaligned_depth"] > 0
     assert plan(4097, 14337, 16, mfma=-1).info["mfma_unaligned_depth"] == 0
     assert plan(4097, 14337, 16, unroll=2).info["mfma_unaligned_depth"] == 0
