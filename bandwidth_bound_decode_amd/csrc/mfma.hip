@@ -4,8 +4,11 @@
 // v_dot2 instructions, so their time grows with M (about 0.6 us per extra vector at
 // 4096 x 14336: 19.9 us at M = 2, 24.4 at 8, 28.3 at 16). Here one v_mfma_f32_16x16x32_bf16
 // takes 16 weight rows (A operand) and 16 input vectors (B operand) over 32 K elements, so
-// the arithmetic per weight byte does not grow with M (19.3 us at M = 2, 19.8 at 8). Batches
+// the arithmetic per weight byte does not grow with M (19.4 us at M = 2, 19.8 at 8). Batches
 // below 16 repeat vectors in the unused B columns, whose outputs are never stored.
+//
+// Two kernels: gemv_mfma for aligned single-matrix calls (below), and gemv_mfma_unaligned
+// (at the end) for calls whose W or x rows are off the 16-byte grid, from M = 10.
 //
 // Operand layout of the 16x16x32 bf16 MFMA on gfx950 (checked on the device against an
 // exact integer product): lane l holds A[l % 16][8 (l / 16) .. +8) and B[8 (l / 16) .. +8)
