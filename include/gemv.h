@@ -204,7 +204,10 @@ void gemv_plan_destroy(gemv_plan_t p);
  * workgroup of its row block to finish, inside the same launch (no second kernel).
  * When W and X are 16-byte aligned with ldw and ldx multiples of 8 the fast path runs
  * (one 16-byte load per lane per row step); any other layout runs the unaligned path,
- * which gives a result within the same tolerance but not bitwise equal to the fast path.
+ * which gives a result within the same tolerance but not bitwise equal to the fast path
+ * (for a plan with mfma_unaligned_depth > 0, on the matrix cores: rows c, c + C, ... with
+ * C = 8 / gcd(ldw, 8) share one offset from the 16-byte grid and are tiled as one aligned
+ * matrix).
  */
 gemv_status gemv_run(gemv_plan_t p,
                      const void *W, int64_t ldw,
