@@ -317,6 +317,9 @@ def test_mfma_plans():
     assert plan(4096, 29823, 16).info["mfma_unaligned_depth"] == 160  # the longest row
     assert plan(4096, 29824, 16).info["mfma_unaligned_depth"] == 0
     assert plan(4097, 14337, 1).info["mfma_unaligned_depth"] == 0
+    small = (128, 8.0e12, 1.0e-6)                                     # 128 CUs: 2048 rows do
+    assert plan(2048, 14337, 16, desc=small).info["mfma_unaligned_depth"] > 0
+    assert plan(2047, 14337, 16, desc=small).info["mfma_unaligned_depth"] == 0
     long_k = plan(64, 1 << 19, 16).info                       # accuracy forces the split
     assert long_k["mfma"] == 1 and long_k["mfma_depth_bound"] <= 160
     with pytest.raises(bbd.GemvError):
