@@ -100,17 +100,20 @@ def test_decode_step_full():
 
 def test_unaligned_and_matrix_core_calls_in_graph():
     """Unaligned calls on the class-staged kernel (x staged whole, x past 64 KiB of LDS, x in
-    chunks) and a matrix-core batch, captured together: every replay bitwise equal to the
-    eager run, and the eager run within tolerance of the oracle."""
+    chunks), a matrix-core batch and an unaligned batch on the matrix cores, captured
+    together: every replay bitwise equal to the eager run, and the eager run within
+    tolerance of the oracle."""
     drawn = []
     for i, (n, k, m, ldw, off) in enumerate([(1000, 14337, 1, 14339, 1), (513, 14337, 4, 14337, 3),
-                                             (300, 14337, 9, 14340, 1), (4096, 4096, 8, 4096, 0)]):
+                                             (300, 14337, 9, 14340, 1), (4096, 4096, 8, 4096, 0),
+                                             (4097, 14337, 16, 14337, 1)]):
         w, x = draw(n, k, m, seed=70 + i)
         W = device_matrix(w, ld=ldw, offset=off)
         X = device_matrix(x, ld=k + (off & 1), offset=off & 1)
         drawn.append((None, [W], X))
     seq = make_sequence(drawn)
-    assert seq.calls[-1].plan.info["mfma"], "want a matrix-core call in the graph"
+    assert seq.calls[3].plan.info["mfma"], "want a matrix-core call in the graph"
+    assert seq.calls[4].plan.info["mfma_unaligned_depth"], "want an unaligned one on them"
     eager = replay_matches_eager(seq)
     for (_, parts, x), y in zip(drawn, eager):
         oracle_check(parts[0], x, y, "unaligned graph")
