@@ -852,7 +852,6 @@ const void *find_fast(int m, int r, int u, bool split, bool multi)
 
 gemv_status device_error(hipError_t e) { return record_hip_error((int)e, GEMV_ERR_DEVICE); }
 
-constexpr size_t kShiftMaxLds = 128 * 1024;   // staged x for the class-staged unaligned kernel
 
 // Launch an unsplit single-matrix unaligned call on gemv_unaligned_lds; *done tells whether
 // it did. The staged chunk of x is the whole row when the M rows fit in kShiftMaxLds, else

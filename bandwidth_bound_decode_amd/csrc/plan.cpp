@@ -509,13 +509,17 @@ extern "C" gemv_status gemv_plan_for(gemv_plan_t *out, int64_t n, int64_t k, int
     }
 
     // Unaligned single-matrix calls on the matrix cores (decided per call: the layout is
-    // the call's): from kMfmaUnalignedMinBatch by default, with every tile option left to
-    // the plan, rows enough for the CUs and the kernel's chain within the depth bound.
+    // the call's): from kMfmaUnalignedMinBatch by default (kMfmaUnalignedStagedMinBatch
+    // where the VALU kernel stages x whole over many rows per CU), with every tile option
+    // left to the plan, rows enough for the CUs and the kernel's chain within the depth bound.
     int mf_unal = 0;
     {
         const bool forced = o.splits || o.rows_per_wave || o.waves_per_block || o.unroll ||
                             o.waves_per_cu;
-        const bool want = o.mfma > 0 ? m >= 2 : o.mfma == 0 && m >= kMfmaUnalignedMinBatch && !forced;
+        const bool x_whole = (k / kVecElems) * m * 16 <= kShiftMaxLds;
+        const bool many_rows = n >= kMfmaUnalignedManyRowsPerCU * dev->compute_units;
+        const int min_m = x_whole && many_rows ? kMfmaUnalignedStagedMinBatch : kMfmaUnalignedMinBatch;
+        const bool want = o.mfma > 0 ? m >= 2 : o.mfma == 0 && m >= min_m && !forced;
         const int depth = mfma_unaligned_depth_for(k);
         if (want && n >= (int64_t)kMfmaUnalignedRowsPerCU * dev->compute_units &&
             depth <= kMaxDepth)

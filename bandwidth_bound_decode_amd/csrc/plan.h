@@ -90,6 +90,15 @@ constexpr int kMfmaMinBatch = 2;
 // kMfmaUnalignedRowsPerCU rows per CU so that its 16-row tiles cover the CUs.
 constexpr int kMfmaUnalignedMinBatch = 10;
 constexpr int kMfmaUnalignedRowsPerCU = 16;
+// ...but from kMfmaUnalignedStagedMinBatch where the class-staged VALU kernel stages the M
+// shifted x rows whole (within kShiftMaxLds) and has at least kMfmaUnalignedManyRowsPerCU rows
+// per CU to amortize that staging over (measured at 28673 x 4097: M = 10 71.7 us on the
+// matrix cores against 67.4 us, 12 76.1 against 76.7, 14 78.1 against 100.6).
+constexpr int kMfmaUnalignedStagedMinBatch = 12;
+constexpr int64_t kMfmaUnalignedManyRowsPerCU = 64;
+// x staged in LDS by the class-staged unaligned kernel: the whole rows up to this many bytes,
+// in chunks beyond.
+constexpr int64_t kShiftMaxLds = 128 * 1024;
 constexpr int kMfmaUnalignedChunk = 128;
 // INT4 weights (int4.hip): 32 weights per 16-byte vector, one bf16 scale per 128.
 constexpr int kInt4VecElems = 32;

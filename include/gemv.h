@@ -147,10 +147,11 @@ typedef struct {
                                CUs with M K <= 14 * 14336; chunks of 128 K elements) or 32
                                (chunks of 64); 0 without the matrix-core launch */
     int mfma_unaligned_depth;   /* > 0 when single-matrix calls whose W or x rows are off the
-                               16-byte grid run on the matrix cores (M >= 10 by default,
-                               M >= 2 with mfma = 1; N >= 16 rows per CU; no tile option
-                               forced): h for that kernel; 0 when they take the VALU
-                               kernels */
+                               16-byte grid run on the matrix cores (M >= 10 by default, or
+                               M >= 12 where the M x rows fit 128 KiB and N >= 64 rows per
+                               CU; M >= 2 with mfma = 1; N >= 16 rows per CU; no tile
+                               option forced): h for that kernel; 0 when they take the
+                               VALU kernels */
 } gemv_plan_info;
 
 /*

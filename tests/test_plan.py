@@ -317,6 +317,11 @@ def test_mfma_plans():
     assert plan(4096, 29823, 16).info["mfma_unaligned_depth"] == 160  # the longest row
     assert plan(4096, 29824, 16).info["mfma_unaligned_depth"] == 0
     assert plan(4097, 14337, 1).info["mfma_unaligned_depth"] == 0
+    # x staged whole by the VALU kernel over >= 64 rows per CU: from M = 12
+    assert plan(28673, 4097, 11).info["mfma_unaligned_depth"] == 0
+    assert plan(28673, 4097, 12).info["mfma_unaligned_depth"] > 0
+    assert plan(14337, 4097, 10).info["mfma_unaligned_depth"] > 0   # 56 rows per CU
+    assert plan(28673, 14337, 10).info["mfma_unaligned_depth"] > 0  # x staged in chunks
     small = (128, 8.0e12, 1.0e-6)                                     # 128 CUs: 2048 rows do
     assert plan(2048, 14337, 16, desc=small).info["mfma_unaligned_depth"] > 0
     assert plan(2047, 14337, 16, desc=small).info["mfma_unaligned_depth"] == 0
