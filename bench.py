@@ -537,8 +537,9 @@ def bench_shards(torch, bbd, workloads, steps, replays):
     return out
 
 
-def cpu_baseline(w, x, runs=3):
-    """The oracle as it stands, on all host threads, over the same full GEMV."""
+def cpu_baseline(w, x, min_seconds=10.0, max_runs=20000):
+    """The oracle as it stands, on all host threads, over the same full GEMV, run back to back
+    for about `min_seconds` of CPU work (a bounded sample); the median run, and the count."""
     import oracle
     import numpy as np
     wb = w.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
@@ -546,12 +547,12 @@ def cpu_baseline(w, x, runs=3):
     threads = oracle.threads(0)
     oracle.gemv(wb, xb, nthreads=threads)                 # untimed warm-up
     times = []
-    for _ in range(runs):
+    start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - start < min_seconds and len(times) < max_runs):
         t0 = time.perf_counter()
         oracle.gemv(wb, xb, nthreads=threads)
         times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return t, threads
+    return statistics.median(times), threads, len(times), time.perf_counter() - start
 
 
 def read_calibration(torch, bbd, cus, steps, window_launches):
@@ -810,14 +811,16 @@ def main(argv=None):
             f"{out['pct_of_read_ceiling']:.1f} % of the ceiling")
 
     if "cpu" in wanted:
-        t_cpu, threads = cpu_baseline(w, x)
+        t_cpu, threads, runs, spent = cpu_baseline(w, x)
         out["cpu_baseline"] = {"value": round(nb / t_cpu / 1e12, 6), "unit": "TB/s",
                                "cores": threads, "kind": "oracle",
-                               "sample": "the full 4096x14336 batch-1 GEMV, fp64 C oracle "
-                                         "(OpenMP over rows), median of 3 runs after 1 warm-up",
-                               "seconds_per_gemv": round(t_cpu, 4),
+                               "sample": f"the full 4096x14336 batch-1 GEMV, fp64 C oracle "
+                                         f"(OpenMP over rows), run {runs} times back to back "
+                                         f"({spent:.1f} s) after 1 warm-up; the median run",
+                               "seconds_per_gemv": round(t_cpu, 5), "runs": runs,
                                "host_cpus": len(os.sched_getaffinity(0))}
-        log(f"cpu oracle: {t_cpu * 1e3:.1f} ms per GEMV on {threads} threads")
+        log(f"cpu oracle: {t_cpu * 1e3:.2f} ms per GEMV on {threads} threads "
+            f"({runs} runs, {spent:.1f} s)")
         out["cpu_baseline"]["per_config"] = oracle_per_config(workloads)
 
     if "shapes" in wanted:
