@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import bandwidth_bound_decode_amd as bbd
-from gpu_helpers import bits_equal, device_matrix, draw, gemv, oracle_check
+from gpu_helpers import bits_equal, device_matrix, draw, gemv, oracle_check, output
 
 pytestmark = pytest.mark.gpu
 
@@ -173,3 +173,26 @@ def test_unaligned_rows_on_the_matrix_cores(n, k, m, ldw, woff, ldx, xoff):
     oracle_check(W, X, Yv, what + " (VALU)")
     if k >= 1024:   # another summation order: some outputs round differently
         assert not bits_equal(Y, Yv), "the matrix-core kernel did not run"
+
+
+def test_unaligned_rows_through_every_entry_point():
+    """The same unaligned batch through gemv_run (with a strided Y), gemv_fused_run with one
+    segment and gemv_run_static (no workspace): all run the matrix-core kernel for unaligned
+    rows and agree bit for bit."""
+    n, k, m = 4100, 6001, 12
+    w, x = draw(n, k, m, seed=4242)
+    W = device_matrix(w, ld=6003, offset=1)
+    X = device_matrix(x, ld=6005, offset=1)
+    p = bbd.Plan(n, k, m)
+    assert p.info["mfma_unaligned_depth"] > 0, p.info
+    Y, _ = gemv(W, X, plan=p, ldy=n + 5)
+    oracle_check(W, X, Y, "unaligned mfma, strided Y")
+    Yf = output(m, n)
+    bbd.fused_run(p, [(W, Yf)], X, p.alloc_workspace())
+    Ys = output(m, n)
+    bbd.run_static(p, W, X, Ys)
+    torch.cuda.synchronize()
+    assert bits_equal(Yf, Y), "fused run differs"
+    assert bits_equal(Ys, Y), "static run differs"
+    Yv, _ = gemv(W, X, mfma=-1)
+    assert not bits_equal(Y, Yv), "the matrix-core kernel did not run"
